@@ -1,0 +1,225 @@
+/*
+ * pa.h — paged-attention decode for AMD Instinct MI355X (gfx950, CDNA4).
+ *
+ * A few query tokens per sequence attend over a KV cache that lives in
+ * fixed-size physical pages reached through a block table, with grouped query
+ * heads, an online softmax, causal masking of the appended query tokens,
+ * optional fp8 (OCP E4M3FN) KV with per-token-head or per-tensor scales, a
+ * split-KV partition pass with a log-sum-exp reduce, and a persistent grid
+ * that walks a work list built by pa_plan().
+ *
+ * Where each operation is defined (the pages give names and behaviour, not
+ * formulas; the plainest reading is stated beside each call):
+ *   [P1] "Benchmark high-perf Paged Attention (#899) vs PA unroll on a2a3",
+ *        hw-native-sys/simpler issue #998, table "Same-Shape Side-by-Side"
+ *        (shape keys b/h/kv/s/bs/hd: batch, query heads, kv heads, context,
+ *        page size, head dim).
+ *   [P2] Ascend/RecSDK issue #1281, HSTU paged attention: section "背景与优化
+ *        特性" (background: history K/V read page by page from the paged KV
+ *        cache), "优化方案" (double-buffered page copies), "其他相关讨论"
+ *        (correctness vs a CPU FP32 reference at rtol = atol = 8e-3) and
+ *        "接口、兼容性与回退" (interface unchanged).
+ *   [P3] "[Kernel][Perf] Optimize paged-attention metadata decode", ROCm/FlyDSL
+ *        PR #910: "Pull request overview" (metadata scheduler, persistent
+ *        decode, split reduction kernel, per-token KV scales, rejection of
+ *        unsupported block sizes and dtypes), the code excerpt (grid = CU
+ *        count x multiplier; the cache's leading dimension is the block
+ *        count), "Summary" (one grid per CU by default) and "Breaking Changes".
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers owned by the caller (for example
+ *     PyTorch tensors); the library allocates no device memory and keeps no
+ *     state beyond a cached CU count per device.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the legacy default
+ *     stream). Every call except pa_plan_status is asynchronous on it.
+ *   - Return value: PA_OK (0) or a negative PA_ERR_* code; pa_last_error()
+ *     gives a thread-local text for the last failure. Argument errors are
+ *     found on the host before any HIP call. Nothing throws across the ABI.
+ *
+ * Layouts (row-major, contiguous):
+ *   q, out          [batch, q_len, num_q_heads, head_dim]      bf16
+ *   k_cache,v_cache [num_pages, num_kv_heads, page_size, head_dim]
+ *                   bf16, or one E4M3FN byte per element
+ *   block_table     [batch, max_pages_per_seq]                 int32
+ *   context_lens    [batch]                                    int32
+ *   kv_scales       per tensor: [2] float32 (K scale, V scale)
+ *                   per token and head: [2][num_pages][num_kv_heads][page_size]
+ *                   float32 (K scales, then V scales)
+ * context_lens[b] counts the q_len appended tokens, whose K/V are already in
+ * the cache; query i of sequence b sees keys t <= context_lens[b] - q_len + i.
+ * Query head h reads kv head h / (num_q_heads / num_kv_heads).
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+enum {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,          /* a required pointer is NULL                  */
+  PA_ERR_ALIGN = -2,         /* a pointer is not aligned as documented      */
+  PA_ERR_DIMS = -3,          /* non-positive size, Hq % Hkv != 0, ...       */
+  PA_ERR_UNSUPPORTED = -4,   /* page size / head dim / dtype / row count the
+                                kernels do not handle ([P3] overview: such
+                                shapes are rejected, not run)               */
+  PA_ERR_WORKSPACE = -5,     /* workspace NULL, too small or misaligned     */
+  PA_ERR_PLAN_MISMATCH = -6, /* plan not built, or q_len / scale mode differ */
+  PA_ERR_SCALE_MODE = -7,    /* bf16 KV with scales, fp8 KV without, or the
+                                scale pointer disagrees with the mode       */
+  PA_ERR_HIP = -8,           /* a HIP runtime call or launch failed         */
+  PA_ERR_DEVICE = -9         /* no usable gfx950 device                     */
+};
+
+/* Bits of the device status word (pa_plan_status). */
+enum {
+  PA_DEV_BAD_CONTEXT = 1,    /* some context_lens[b] outside
+                                [max(1, q_len), max_pages_per_seq * page_size];
+                                the plan is then empty and decode writes
+                                nothing                                      */
+  PA_DEV_BAD_PAGE = 2        /* a block-table entry outside [0, num_pages)
+                                (checked only with PA_FLAG_DEBUG_BOUNDS; such
+                                tokens are then read as zeros)               */
+};
+
+enum { PA_KV_BF16 = 0, PA_KV_FP8_E4M3FN = 1 };
+enum { PA_SCALE_NONE = 0, PA_SCALE_PER_TENSOR = 1, PA_SCALE_PER_TOKEN_HEAD = 2 };
+enum { PA_FLAG_DEBUG_BOUNDS = 1 };
+
+/* Problem description. Zero in partition_size / grid_multiplier selects the
+ * default (256 tokens; one persistent workgroup per CU, [P3] "Summary"). */
+typedef struct pa_dims {
+  int32_t batch;
+  int32_t q_len;               /* appended query tokens per sequence, >= 1   */
+  int32_t num_q_heads;
+  int32_t num_kv_heads;        /* divides num_q_heads                        */
+  int32_t head_dim;            /* 128 or 256                                 */
+  int32_t page_size;           /* power of two in [16, 1024]                 */
+  int32_t num_pages;           /* k_cache.shape[0] ([P3] code excerpt)       */
+  int32_t max_pages_per_seq;   /* block_table row stride                     */
+  int32_t kv_dtype;            /* PA_KV_*                                    */
+  int32_t kv_scale_mode;       /* PA_SCALE_*                                 */
+  int32_t partition_size;      /* tokens per work item, multiple of 16       */
+  int32_t grid_multiplier;     /* persistent workgroups per CU, 1..16        */
+  int32_t flags;               /* PA_FLAG_*                                  */
+} pa_dims;
+
+/* A built plan: caller-owned plain data, filled by pa_plan(). It points into
+ * the caller's workspace, which must stay alive and must not be shared by
+ * two streams until the decode that uses it has finished. */
+typedef struct pa_plan_t {
+  uint32_t magic;              /* set by pa_plan                             */
+  int32_t device;              /* HIP device the plan was built on           */
+  pa_dims dims;                /* validated copy, defaults applied           */
+  int32_t num_cus;             /* hipDeviceAttributeMultiprocessorCount      */
+  int32_t grid;                /* num_cus * grid_multiplier                  */
+  int32_t rows;                /* q_len * (num_q_heads / num_kv_heads)       */
+  int32_t num_pairs;           /* batch * num_kv_heads                       */
+  int32_t max_items;           /* capacity of the item list                  */
+  int32_t max_segs;            /* capacity of the segment list (= max slots) */
+  int32_t variant;             /* decode kernel instantiation chosen         */
+  int32_t reserved0;
+  void* workspace;
+  uint64_t workspace_bytes;
+  /* byte offsets into the workspace (all 256-byte aligned) */
+  uint64_t off_status;         /* int32[4]: status bits, N items, N segments */
+  uint64_t off_wg_begin;       /* int32[grid + 1]: item range per workgroup  */
+  uint64_t off_wg_seg_begin;   /* int32[grid + 1]: segment range per wg      */
+  uint64_t off_items;          /* int32[max_items][4]: pair, tok_begin,
+                                  tok_end, slot                              */
+  uint64_t off_segs;           /* int32[max_segs][4]: same fields, one per
+                                  segment, in workgroup order                */
+  uint64_t off_nseg;           /* int32[num_pairs]                           */
+  uint64_t off_seg_base;       /* int32[num_pairs + 1] (split pairs' slots)  */
+  uint64_t off_pseg_base;      /* int32[num_pairs + 1] (all segments)        */
+  uint64_t off_batch_base;     /* int32[batch + 1]: first item of sequence b */
+  uint64_t off_partial_lse;    /* float[max_segs][rows]                      */
+  uint64_t off_partial_o;      /* float[max_segs][rows][head_dim]            */
+  uint64_t reserved[4];
+} pa_plan_t;
+
+#define PA_PLAN_MAGIC 0x50414450u
+
+/* Number of compute units of HIP device `device` (cached after the first
+ * call). Errors: PA_ERR_NULL, PA_ERR_DEVICE. */
+int pa_query_device(int32_t device, int32_t* num_cus);
+
+/* Workspace bytes a plan for `dims` on a device with `num_cus` CUs needs.
+ * Host-only; validates dims exactly as pa_plan does. Errors: PA_ERR_NULL,
+ * PA_ERR_DIMS, PA_ERR_UNSUPPORTED, PA_ERR_SCALE_MODE. */
+int pa_workspace_bytes(const pa_dims* dims, int32_t num_cus, uint64_t* bytes);
+
+/* Build the persistent work list on the current HIP device ([P3] overview:
+ * "metadata scheduler"; code excerpt: grid = CUs x multiplier). Launches one
+ * workgroup that reads context_lens (device int32[batch]) and writes into
+ * `workspace` (device, 256-byte aligned, >= pa_workspace_bytes):
+ *   items   for b, then kv head g, then partition k < ceil(ctx_b / P):
+ *           (b * Hkv + g, k * P, min((k + 1) * P, ctx_b), slot)
+ *   ranges  workgroup w owns items [floor(w N / G), floor((w + 1) N / G))
+ *   segments maximal same-pair runs inside one range; a pair with one
+ *           segment is finished by its workgroup, the segments of a split
+ *           pair get partial slots seg_base[pair] + their index
+ * and fills *plan. Invalid context lengths set PA_DEV_BAD_CONTEXT in the
+ * device status word and give an empty plan. Asynchronous. Errors:
+ * PA_ERR_NULL, PA_ERR_DIMS, PA_ERR_UNSUPPORTED, PA_ERR_SCALE_MODE,
+ * PA_ERR_WORKSPACE, PA_ERR_ALIGN, PA_ERR_DEVICE, PA_ERR_HIP. */
+int pa_plan(const pa_dims* dims, const int32_t* context_lens, void* workspace,
+            uint64_t workspace_bytes, pa_plan_t* plan, void* stream);
+
+/* Decode attention for every (sequence, query, head): the partition pass
+ * over the plan's segments, then the log-sum-exp reduce of split pairs
+ * ([P3] overview: persistent decode + "reduction kernel"; [P2] background:
+ * K/V read from the paged cache through the block table). out (device bf16)
+ * receives softmax(scale * q K^T) V rounded to nearest even, with fp8 K/V
+ * dequantised as byte value x scale. q_len and kv_scale_mode must equal the
+ * plan's; kv_scales must be NULL iff the mode is PA_SCALE_NONE. q, k_cache,
+ * v_cache, out and per-token kv_scales must be 16-byte aligned; block_table,
+ * context_lens and per-tensor kv_scales 4-byte aligned. Asynchronous. Errors:
+ * PA_ERR_NULL, PA_ERR_ALIGN, PA_ERR_PLAN_MISMATCH, PA_ERR_SCALE_MODE,
+ * PA_ERR_HIP. */
+int pa_decode(const pa_plan_t* plan, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_table, const int32_t* context_lens, int32_t q_len,
+              float scale, int32_t kv_scale_mode, const float* kv_scales, void* out,
+              void* stream);
+
+/* The two launches of pa_decode, separately: the partition pass (writes the
+ * output of unsplit pairs and the partials of split ones) and the reduce
+ * (merges the partials). pa_decode == pa_decode_partition then
+ * pa_decode_reduce on the same stream; same arguments and errors. */
+int pa_decode_partition(const pa_plan_t* plan, const void* q, const void* k_cache,
+                        const void* v_cache, const int32_t* block_table,
+                        const int32_t* context_lens, int32_t q_len, float scale,
+                        int32_t kv_scale_mode, const float* kv_scales, void* out,
+                        void* stream);
+int pa_decode_reduce(const pa_plan_t* plan, int32_t q_len, int32_t kv_scale_mode, void* out,
+                     void* stream);
+
+/* Synchronise `stream` and copy the device status word (PA_DEV_* bits) to
+ * *device_status. The only blocking call. Errors: PA_ERR_NULL,
+ * PA_ERR_PLAN_MISMATCH, PA_ERR_HIP. */
+int pa_plan_status(const pa_plan_t* plan, int32_t* device_status, void* stream);
+
+/* Test support: copy the cache rows every (sequence b, kv head g, token
+ * t < ctx_b) reads, through the block table with the decode kernel's own
+ * page addressing, to k_out / v_out laid out [batch][num_kv_heads]
+ * [max_pages_per_seq * page_size][head_dim] (element type of the cache;
+ * rows t >= ctx_b are left untouched). Asynchronous. Errors: as pa_decode. */
+int pa_debug_gather(const pa_plan_t* plan, const void* k_cache, const void* v_cache,
+                    const int32_t* block_table, const int32_t* context_lens, void* k_out,
+                    void* v_out, void* stream);
+
+/* Static text for a PA_* status code. */
+const char* pa_status_string(int status);
+
+/* Thread-local text describing the last failed call on this thread. */
+const char* pa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PA_H */

@@ -1,0 +1,425 @@
+// C-ABI of the paged-attention decode library (declared in include/pa.h).
+//
+// Host work only: argument validation (before any HIP call, so every
+// argument error is reported without a device), workspace layout, the
+// per-device CU count, and kernel launches on the caller's stream. The
+// library allocates no device memory.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+
+#include "pa_common.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return PA_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int log2i(int x) {
+  int r = 0;
+  while ((1 << r) < x) ++r;
+  return r;
+}
+
+constexpr int kDefaultPartition = 256;
+constexpr int kMaxGridMultiplier = 16;
+constexpr int kMaxDevices = 64;
+
+std::mutex g_dev_mu;
+int g_cu_cache[kMaxDevices] = {0};
+
+// Validates dims and applies defaults into *out. Host-only.
+int check_dims(const pa_dims* in, pa_dims* out, int* variant) {
+  if (!in) return fail(PA_ERR_NULL, "dims is NULL");
+  pa_dims d = *in;
+  if (d.partition_size == 0) d.partition_size = kDefaultPartition;
+  if (d.grid_multiplier == 0) d.grid_multiplier = 1;
+  if (d.batch < 1 || d.q_len < 1 || d.num_q_heads < 1 || d.num_kv_heads < 1 || d.num_pages < 1 ||
+      d.max_pages_per_seq < 1)
+    return fail(PA_ERR_DIMS, "batch, q_len, heads, num_pages and max_pages_per_seq must be >= 1");
+  if (d.num_q_heads % d.num_kv_heads != 0)
+    return fail(PA_ERR_DIMS, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)",
+                d.num_q_heads, d.num_kv_heads);
+  if (d.grid_multiplier < 1 || d.grid_multiplier > kMaxGridMultiplier)
+    return fail(PA_ERR_DIMS, "grid_multiplier %d outside [1, %d]", d.grid_multiplier,
+                kMaxGridMultiplier);
+  if (d.flags & ~PA_FLAG_DEBUG_BOUNDS) return fail(PA_ERR_DIMS, "unknown flag bits 0x%x", d.flags);
+  if (d.head_dim != 128 && d.head_dim != 256)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d not supported (128 or 256)", d.head_dim);
+  if (!pow2(d.page_size) || d.page_size < 16 || d.page_size > 1024)
+    return fail(PA_ERR_UNSUPPORTED, "page_size %d not supported (power of two in [16, 1024])",
+                d.page_size);
+  if (d.partition_size < 16 || d.partition_size % 16 != 0 || d.partition_size > (1 << 20))
+    return fail(PA_ERR_UNSUPPORTED, "partition_size %d must be a positive multiple of 16",
+                d.partition_size);
+  if (d.kv_dtype != PA_KV_BF16 && d.kv_dtype != PA_KV_FP8_E4M3FN)
+    return fail(PA_ERR_UNSUPPORTED, "kv_dtype %d not supported", d.kv_dtype);
+  if (d.kv_dtype == PA_KV_BF16 && d.kv_scale_mode != PA_SCALE_NONE)
+    return fail(PA_ERR_SCALE_MODE, "bf16 KV takes no scales (kv_scale_mode must be NONE)");
+  if (d.kv_dtype == PA_KV_FP8_E4M3FN && d.kv_scale_mode != PA_SCALE_PER_TENSOR &&
+      d.kv_scale_mode != PA_SCALE_PER_TOKEN_HEAD)
+    return fail(PA_ERR_SCALE_MODE, "fp8 KV needs PER_TENSOR or PER_TOKEN_HEAD scales");
+  const int64_t capacity = static_cast<int64_t>(d.max_pages_per_seq) * d.page_size;
+  if (capacity > (int64_t(1) << 30)) return fail(PA_ERR_DIMS, "max_pages_per_seq * page_size too large");
+  const int64_t rows = static_cast<int64_t>(d.q_len) * (d.num_q_heads / d.num_kv_heads);
+  const int v = pa::pick_variant(d.head_dim, d.kv_dtype == PA_KV_FP8_E4M3FN, d.kv_scale_mode,
+                                 static_cast<int>(rows > 4096 ? 4096 : rows));
+  if (rows > 4096 || v < 0)
+    return fail(PA_ERR_UNSUPPORTED,
+                "q_len * (num_q_heads / num_kv_heads) = %lld rows per kv head is more than the "
+                "kernels hold for head_dim %d",
+                static_cast<long long>(rows), d.head_dim);
+  const int64_t pairs = static_cast<int64_t>(d.batch) * d.num_kv_heads;
+  const int64_t items = pairs * ((capacity + d.partition_size - 1) / d.partition_size);
+  if (pairs > (1 << 24) || items > (int64_t(1) << 30))
+    return fail(PA_ERR_DIMS, "too many work items (%lld)", static_cast<long long>(items));
+  *out = d;
+  *variant = v;
+  return PA_OK;
+}
+
+struct Layout {
+  uint64_t status, wg_begin, wg_seg_begin, items, segs, nseg, seg_base, pseg_base, batch_base,
+      partial_lse, partial_o, total;
+  int32_t grid, pairs, rows, max_items, max_segs;
+};
+
+uint64_t round256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+
+Layout layout(const pa_dims& d, int num_cus) {
+  Layout L;
+  L.grid = num_cus * d.grid_multiplier;
+  L.pairs = d.batch * d.num_kv_heads;
+  L.rows = d.q_len * (d.num_q_heads / d.num_kv_heads);
+  const int64_t capacity = static_cast<int64_t>(d.max_pages_per_seq) * d.page_size;
+  L.max_items = static_cast<int32_t>(L.pairs * ((capacity + d.partition_size - 1) / d.partition_size));
+  L.max_segs = L.grid + L.pairs;
+  uint64_t off = 0;
+  auto take = [&](uint64_t bytes) {
+    const uint64_t o = off;
+    off = round256(off + bytes);
+    return o;
+  };
+  L.status = take(16);
+  L.wg_begin = take(4ull * (L.grid + 1));
+  L.wg_seg_begin = take(4ull * (L.grid + 1));
+  L.items = take(16ull * L.max_items);
+  L.segs = take(16ull * L.max_segs);
+  L.nseg = take(4ull * L.pairs);
+  L.seg_base = take(4ull * (L.pairs + 1));
+  L.pseg_base = take(4ull * (L.pairs + 1));
+  L.batch_base = take(4ull * (d.batch + 1));
+  L.partial_lse = take(4ull * L.max_segs * L.rows);
+  L.partial_o = take(4ull * L.max_segs * L.rows * d.head_dim);
+  L.total = off;
+  return L;
+}
+
+int current_device(int* dev) {
+  const hipError_t e = hipGetDevice(dev);
+  if (e != hipSuccess) return fail(PA_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+template <typename T>
+T* at(const pa_plan_t* p, uint64_t off) {
+  return reinterpret_cast<T*>(static_cast<uint8_t*>(p->workspace) + off);
+}
+
+int check_plan(const pa_plan_t* plan) {
+  if (!plan) return fail(PA_ERR_NULL, "plan is NULL");
+  if (plan->magic != PA_PLAN_MAGIC) return fail(PA_ERR_PLAN_MISMATCH, "plan was not built by pa_plan");
+  int dev = -1;
+  if (int rc = current_device(&dev)) return rc;
+  if (dev != plan->device)
+    return fail(PA_ERR_PLAN_MISMATCH, "plan was built on device %d, current device is %d",
+                plan->device, dev);
+  return PA_OK;
+}
+
+int check_decode_args(const pa_plan_t* plan, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_table, const int32_t* context_lens, int32_t q_len,
+                      int32_t kv_scale_mode, const float* kv_scales, const void* out) {
+  if (!plan) return fail(PA_ERR_NULL, "plan is NULL");
+  if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out)
+    return fail(PA_ERR_NULL, "q, k_cache, v_cache, block_table, context_lens and out are required");
+  if (plan->magic != PA_PLAN_MAGIC) return fail(PA_ERR_PLAN_MISMATCH, "plan was not built by pa_plan");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16))
+    return fail(PA_ERR_ALIGN, "q, k_cache, v_cache and out must be 16-byte aligned");
+  if (!aligned(block_table, 4) || !aligned(context_lens, 4))
+    return fail(PA_ERR_ALIGN, "block_table and context_lens must be 4-byte aligned");
+  if (q_len != plan->dims.q_len)
+    return fail(PA_ERR_PLAN_MISMATCH, "q_len %d differs from the plan's %d", q_len, plan->dims.q_len);
+  if (kv_scale_mode != plan->dims.kv_scale_mode)
+    return fail(PA_ERR_PLAN_MISMATCH, "kv_scale_mode %d differs from the plan's %d", kv_scale_mode,
+                plan->dims.kv_scale_mode);
+  if ((kv_scale_mode == PA_SCALE_NONE) != (kv_scales == nullptr))
+    return fail(PA_ERR_SCALE_MODE, "kv_scales must be NULL exactly when kv_scale_mode is NONE");
+  if (kv_scale_mode == PA_SCALE_PER_TOKEN_HEAD && !aligned(kv_scales, 16))
+    return fail(PA_ERR_ALIGN, "per-token kv_scales must be 16-byte aligned");
+  if (kv_scale_mode == PA_SCALE_PER_TENSOR && !aligned(kv_scales, 4))
+    return fail(PA_ERR_ALIGN, "per-tensor kv_scales must be 4-byte aligned");
+  return check_plan(plan);
+}
+
+pa::DecodeArgs decode_args(const pa_plan_t* plan, const void* q, const void* k_cache,
+                           const void* v_cache, const int32_t* block_table,
+                           const int32_t* context_lens, float scale, const float* kv_scales,
+                           void* out) {
+  const pa_dims& d = plan->dims;
+  pa::DecodeArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_cache = static_cast<const uint8_t*>(k_cache);
+  a.v_cache = static_cast<const uint8_t*>(v_cache);
+  a.block_table = block_table;
+  a.context_lens = context_lens;
+  a.segs = at<const pa::Span>(plan, plan->off_segs);
+  a.wg_seg_begin = at<const int32_t>(plan, plan->off_wg_seg_begin);
+  a.nseg = at<const int32_t>(plan, plan->off_nseg);
+  a.seg_base = at<const int32_t>(plan, plan->off_seg_base);
+  a.kv_scales = kv_scales;
+  a.out = static_cast<uint16_t*>(out);
+  a.partial_o = at<float>(plan, plan->off_partial_o);
+  a.partial_lse = at<float>(plan, plan->off_partial_lse);
+  a.status = at<int32_t>(plan, plan->off_status);
+  a.batch = d.batch;
+  a.q_len = d.q_len;
+  a.num_q_heads = d.num_q_heads;
+  a.num_kv_heads = d.num_kv_heads;
+  a.group = d.num_q_heads / d.num_kv_heads;
+  a.rows = plan->rows;
+  a.ps_log2 = log2i(d.page_size);
+  a.max_pages = d.max_pages_per_seq;
+  a.num_pages = d.num_pages;
+  a.scale_mode = d.kv_scale_mode;
+  a.debug_bounds = (d.flags & PA_FLAG_DEBUG_BOUNDS) ? 1 : 0;
+  a.qk_scale_log2 = scale * 1.4426950408889634f;
+  a.out_scale = 1.0f;
+  return a;
+}
+
+int hip_check(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_query_device(int32_t device, int32_t* num_cus) {
+  if (!num_cus) return fail(PA_ERR_NULL, "num_cus is NULL");
+  if (device < 0 || device >= kMaxDevices) return fail(PA_ERR_DEVICE, "device %d out of range", device);
+  {
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    if (g_cu_cache[device] > 0) {
+      *num_cus = g_cu_cache[device];
+      return ok();
+    }
+  }
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || device >= count)
+    return fail(PA_ERR_DEVICE, "no HIP device %d", device);
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess)
+    return fail(PA_ERR_DEVICE, "hipGetDeviceProperties(%d) failed", device);
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(PA_ERR_DEVICE, "device %d is %s; this library is built for gfx950 only", device,
+                prop.gcnArchName);
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || n < 1)
+    return fail(PA_ERR_DEVICE, "cannot read the CU count of device %d", device);
+  {
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    g_cu_cache[device] = n;
+  }
+  *num_cus = n;
+  return ok();
+}
+
+int pa_workspace_bytes(const pa_dims* dims, int32_t num_cus, uint64_t* bytes) {
+  if (!bytes) return fail(PA_ERR_NULL, "bytes is NULL");
+  pa_dims d;
+  int v = -1;
+  if (int rc = check_dims(dims, &d, &v)) return rc;
+  if (num_cus < 1 || num_cus > 65536) return fail(PA_ERR_DIMS, "num_cus %d out of range", num_cus);
+  *bytes = layout(d, num_cus).total;
+  return ok();
+}
+
+int pa_plan(const pa_dims* dims, const int32_t* context_lens, void* workspace,
+            uint64_t workspace_bytes, pa_plan_t* plan, void* stream) {
+  pa_dims d;
+  int v = -1;
+  if (int rc = check_dims(dims, &d, &v)) return rc;
+  if (!context_lens || !plan) return fail(PA_ERR_NULL, "context_lens and plan are required");
+  if (!workspace) return fail(PA_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(PA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if (!aligned(context_lens, 4)) return fail(PA_ERR_ALIGN, "context_lens must be 4-byte aligned");
+  int dev = -1;
+  if (int rc = current_device(&dev)) return rc;
+  int32_t cus = 0;
+  if (int rc = pa_query_device(dev, &cus)) return rc;
+  const Layout L = layout(d, cus);
+  if (workspace_bytes < L.total)
+    return fail(PA_ERR_WORKSPACE, "workspace of %llu bytes, %llu needed",
+                static_cast<unsigned long long>(workspace_bytes),
+                static_cast<unsigned long long>(L.total));
+  pa_plan_t p;
+  memset(&p, 0, sizeof(p));
+  p.magic = PA_PLAN_MAGIC;
+  p.device = dev;
+  p.dims = d;
+  p.num_cus = cus;
+  p.grid = L.grid;
+  p.rows = L.rows;
+  p.num_pairs = L.pairs;
+  p.max_items = L.max_items;
+  p.max_segs = L.max_segs;
+  p.variant = v;
+  p.workspace = workspace;
+  p.workspace_bytes = workspace_bytes;
+  p.off_status = L.status;
+  p.off_wg_begin = L.wg_begin;
+  p.off_wg_seg_begin = L.wg_seg_begin;
+  p.off_items = L.items;
+  p.off_segs = L.segs;
+  p.off_nseg = L.nseg;
+  p.off_seg_base = L.seg_base;
+  p.off_pseg_base = L.pseg_base;
+  p.off_batch_base = L.batch_base;
+  p.off_partial_lse = L.partial_lse;
+  p.off_partial_o = L.partial_o;
+
+  pa::PlanArgs a;
+  a.context_lens = context_lens;
+  a.status = at<int32_t>(&p, p.off_status);
+  a.wg_begin = at<int32_t>(&p, p.off_wg_begin);
+  a.wg_seg_begin = at<int32_t>(&p, p.off_wg_seg_begin);
+  a.items = at<pa::Span>(&p, p.off_items);
+  a.segs = at<pa::Span>(&p, p.off_segs);
+  a.nseg = at<int32_t>(&p, p.off_nseg);
+  a.seg_base = at<int32_t>(&p, p.off_seg_base);
+  a.pseg_base = at<int32_t>(&p, p.off_pseg_base);
+  a.batch_base = at<int32_t>(&p, p.off_batch_base);
+  a.batch = d.batch;
+  a.num_kv_heads = d.num_kv_heads;
+  a.q_len = d.q_len;
+  a.partition = d.partition_size;
+  a.grid = L.grid;
+  a.capacity = d.max_pages_per_seq * d.page_size;
+  if (int rc = hip_check(pa::launch_plan(a, static_cast<hipStream_t>(stream)), "plan launch"))
+    return rc;
+  *plan = p;
+  return ok();
+}
+
+int pa_decode_partition(const pa_plan_t* plan, const void* q, const void* k_cache,
+                        const void* v_cache, const int32_t* block_table,
+                        const int32_t* context_lens, int32_t q_len, float scale,
+                        int32_t kv_scale_mode, const float* kv_scales, void* out, void* stream) {
+  if (int rc = check_decode_args(plan, q, k_cache, v_cache, block_table, context_lens, q_len,
+                                 kv_scale_mode, kv_scales, out))
+    return rc;
+  const pa::DecodeArgs a =
+      decode_args(plan, q, k_cache, v_cache, block_table, context_lens, scale, kv_scales, out);
+  return hip_check(pa::launch_partition(plan->variant, a, plan->grid, static_cast<hipStream_t>(stream)),
+                   "partition launch") ?: ok();
+}
+
+int pa_decode_reduce(const pa_plan_t* plan, int32_t q_len, int32_t kv_scale_mode, void* out,
+                     void* stream) {
+  if (!plan || !out) return fail(PA_ERR_NULL, "plan and out are required");
+  if (plan->magic != PA_PLAN_MAGIC) return fail(PA_ERR_PLAN_MISMATCH, "plan was not built by pa_plan");
+  if (!aligned(out, 16)) return fail(PA_ERR_ALIGN, "out must be 16-byte aligned");
+  if (q_len != plan->dims.q_len || kv_scale_mode != plan->dims.kv_scale_mode)
+    return fail(PA_ERR_PLAN_MISMATCH, "q_len / kv_scale_mode differ from the plan's");
+  if (int rc = check_plan(plan)) return rc;
+  pa::DecodeArgs a = decode_args(plan, out, out, out, nullptr, nullptr, 1.0f, nullptr, out);
+  return hip_check(pa::launch_reduce(a, plan->dims.head_dim, plan->num_pairs,
+                                     static_cast<hipStream_t>(stream)),
+                   "reduce launch") ?: ok();
+}
+
+int pa_decode(const pa_plan_t* plan, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_table, const int32_t* context_lens, int32_t q_len, float scale,
+              int32_t kv_scale_mode, const float* kv_scales, void* out, void* stream) {
+  if (int rc = pa_decode_partition(plan, q, k_cache, v_cache, block_table, context_lens, q_len,
+                                   scale, kv_scale_mode, kv_scales, out, stream))
+    return rc;
+  return pa_decode_reduce(plan, q_len, kv_scale_mode, out, stream);
+}
+
+int pa_plan_status(const pa_plan_t* plan, int32_t* device_status, void* stream) {
+  if (!device_status) return fail(PA_ERR_NULL, "device_status is NULL");
+  if (int rc = check_plan(plan)) return rc;
+  if (int rc = hip_check(hipStreamSynchronize(static_cast<hipStream_t>(stream)), "hipStreamSynchronize"))
+    return rc;
+  int32_t st = 0;
+  if (int rc = hip_check(hipMemcpy(&st, at<int32_t>(plan, plan->off_status), sizeof(st),
+                                   hipMemcpyDeviceToHost),
+                         "hipMemcpy status"))
+    return rc;
+  *device_status = st;
+  return ok();
+}
+
+int pa_debug_gather(const pa_plan_t* plan, const void* k_cache, const void* v_cache,
+                    const int32_t* block_table, const int32_t* context_lens, void* k_out,
+                    void* v_out, void* stream) {
+  if (!plan || !k_cache || !v_cache || !block_table || !context_lens || !k_out || !v_out)
+    return fail(PA_ERR_NULL, "every pointer is required");
+  if (plan->magic != PA_PLAN_MAGIC) return fail(PA_ERR_PLAN_MISMATCH, "plan was not built by pa_plan");
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(k_out, 16) || !aligned(v_out, 16))
+    return fail(PA_ERR_ALIGN, "caches and outputs must be 16-byte aligned");
+  if (int rc = check_plan(plan)) return rc;
+  const pa_dims& d = plan->dims;
+  pa::DecodeArgs a = decode_args(plan, k_cache, k_cache, v_cache, block_table, context_lens, 1.0f,
+                                 nullptr, k_out);
+  const int elt = d.kv_dtype == PA_KV_FP8_E4M3FN ? 1 : 2;
+  return hip_check(pa::launch_gather(a, d.head_dim, elt, d.max_pages_per_seq * d.page_size,
+                                     static_cast<uint8_t*>(k_out), static_cast<uint8_t*>(v_out),
+                                     static_cast<hipStream_t>(stream)),
+                   "gather launch") ?: ok();
+}
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_NULL: return "PA_ERR_NULL: a required pointer is NULL";
+    case PA_ERR_ALIGN: return "PA_ERR_ALIGN: a pointer is misaligned";
+    case PA_ERR_DIMS: return "PA_ERR_DIMS: invalid dimensions";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: shape or dtype not supported";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
+    case PA_ERR_PLAN_MISMATCH: return "PA_ERR_PLAN_MISMATCH: call does not match the plan";
+    case PA_ERR_SCALE_MODE: return "PA_ERR_SCALE_MODE: kv dtype and scale mode disagree";
+    case PA_ERR_HIP: return "PA_ERR_HIP: HIP runtime error";
+    case PA_ERR_DEVICE: return "PA_ERR_DEVICE: no usable gfx950 device";
+    default: return "unknown status";
+  }
+}
+
+const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,647 @@
+// Paged-attention decode kernels for gfx950: the persistent partition pass,
+// the log-sum-exp reduce of split pairs, and a debug gather that shares the
+// partition pass's page addressing.
+//
+// What the pages fix: the KV cache is read page by page through a block
+// table (Ascend/RecSDK issue #1281, section "背景与优化特性", background);
+// overlapping the next chunk's page loads with the work on the current one
+// is the optimisation that issue makes (section "优化方案": K/V double
+// buffering); the decode is persistent over a metadata work list and split
+// pieces are merged by a reduction kernel, with per-token or per-tensor fp8 KV
+// scales ("[Kernel][Perf] Optimize paged-attention metadata decode", ROCm/
+// FlyDSL PR #910, "Pull request overview"); grouped query heads share a kv
+// head ("h16_kv1", hw-native-sys/simpler issue #998, table "Same-Shape
+// Side-by-Side"). The arithmetic is scaled-dot-product softmax attention, the
+// plainest reading of "paged attention decode".
+//
+// Partition pass, one workgroup of NW waves per persistent slot:
+//   * the workgroup walks its segments (token ranges of one (sequence, kv
+//     head) pair); inside a segment wave w takes chunks w, w + NW, ... of
+//     TC = 16 * NB tokens
+//   * each wave runs a three-stage software pipeline over its chunk stream:
+//     block-table entries two chunks ahead (scalar loads), K/V rows one chunk
+//     ahead (16-byte vector loads straight into MFMA operand registers), and
+//     the math on the current chunk
+//   * S^T = K Q^T on MFMA 16x16x32 bf16 (K rows are the A operand as loaded;
+//     fp8 K is decoded to bf16 exactly); fp32 online softmax in the exp2
+//     domain with the causal mask of the appended tokens; O^T += V^T P^T on
+//     MFMA, where P^T comes lane-locally from S^T and V^T is read from a
+//     wave-private LDS tile (V rows written row-major, read transposed)
+//   * at a segment's end the NW waves merge their (max, sum, O) through LDS;
+//     an unsplit pair writes bf16 output, a split pair writes its partial O
+//     and log-sum-exp to its slot
+#include "pa_common.h"
+
+namespace pa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+__device__ __forceinline__ u32x4 ld16(const uint8_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+// 8 E4M3FN bytes -> 8 bf16 (exact: every finite E4M3FN value is a bf16 value).
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
+  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(lo), false);
+  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(lo), true);
+  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(hi), false);
+  const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(hi), true);
+  const f32x8 f = {a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+  return __builtin_convertvector(f, bf16x8);
+}
+
+template <int D, bool FP8, int RT, int NB, int NW>
+struct Cfg {
+  static constexpr int KVB = FP8 ? 1 : 2;      // bytes per cache element
+  static constexpr int ROWB = D * KVB;         // bytes per cache row
+  static constexpr int LPB = ROWB / 64;        // 16-B loads per lane per 16-token block
+  static constexpr int KC = D / 32;            // MFMA k-steps over head_dim
+  static constexpr int DT = D / 16;            // 16-dim tiles of the output
+  static constexpr int TC = 16 * NB;           // tokens per chunk
+  static constexpr int VROW = 2 * D + 8;       // bytes per V row in LDS (bank spread)
+  static constexpr int VBYTES = TC * VROW;
+  static constexpr int OROW = D + 4;           // floats per row of the merge tile
+  static constexpr int OBYTES = 16 * OROW * 4;
+  static constexpr int WBYTES = VBYTES > OBYTES ? VBYTES : OBYTES;
+  static constexpr int THREADS = NW * 64;
+  static_assert(ROWB % 64 == 0, "row must be a multiple of 64 bytes");
+  static_assert(NB == 1 || NB % 2 == 0, "blocks per chunk: 1 or even");
+};
+
+// head_dim index of the first of the 8 contiguous dims that lane group j
+// feeds to QK^T k-step kc. bf16 rows are loaded 16 B = 8 dims at a time; fp8
+// rows 16 B = 16 dims, split into two k-steps. The same map orders Q.
+template <bool FP8>
+__device__ __forceinline__ constexpr int qk_dim(int kc, int j) {
+  return FP8 ? 64 * (kc >> 1) + 16 * j + 8 * (kc & 1) : 32 * kc + 8 * j;
+}
+
+template <int D, bool FP8, int NB, int SM>
+struct Stage {
+  static constexpr int LPB = D * (FP8 ? 1 : 2) / 64;
+  static constexpr int NS = SM == PA_SCALE_PER_TOKEN_HEAD ? NB : 0;
+  u32x4 k[NB][LPB];
+  u32x4 v[NB][LPB];
+  f32x4 ks[NS > 0 ? NS : 1];  // per-token K scales of the lane's S^T tokens
+  f32x4 vs[NS > 0 ? NS : 1];
+};
+
+// One entry of a wave's chunk stream (wave-uniform values).
+struct Entry {
+  int32_t live;           // entry exists
+  int32_t first, last;    // first / last entry of this wave in its segment
+  int32_t data;           // the chunk holds tokens (else: merge only)
+  int32_t b, g, ctx, te, slot, tc0;
+};
+
+struct Cursor {
+  int32_t s, s_end, k;
+  int32_t b, g, ctx, tb, te, slot;
+  int32_t live;
+};
+
+__device__ __forceinline__ void cursor_load(Cursor& c, const DecodeArgs& a, int wave) {
+  const Span sp = a.segs[c.s];
+  c.b = sp.pair / a.num_kv_heads;
+  c.g = sp.pair - c.b * a.num_kv_heads;
+  c.tb = sp.tok_begin;
+  c.te = sp.tok_end;
+  c.slot = sp.slot;
+  c.ctx = a.context_lens[c.b];
+  c.k = wave;
+}
+
+template <int TC, int NW>
+__device__ __forceinline__ Entry cursor_take(Cursor& c, const DecodeArgs& a, int wave) {
+  Entry e;
+  e.live = c.live;
+  if (!c.live) {
+    e.first = e.last = e.data = 0;
+    e.b = e.g = e.ctx = e.te = e.slot = e.tc0 = 0;
+    return e;
+  }
+  e.b = c.b;
+  e.g = c.g;
+  e.ctx = c.ctx;
+  e.te = c.te;
+  e.slot = c.slot;
+  e.tc0 = c.tb + TC * c.k;
+  e.data = e.tc0 < c.te;
+  e.first = c.k == wave;
+  e.last = !e.data || c.tb + TC * (c.k + NW) >= c.te;
+  if (!e.last) {
+    c.k += NW;
+  } else if (++c.s < c.s_end) {
+    cursor_load(c, a, wave);
+  } else {
+    c.live = 0;
+  }
+  return e;
+}
+
+template <int NB>
+__device__ __forceinline__ void load_pages(const DecodeArgs& a, const Entry& e, int32_t (&pg)[NB]) {
+#pragma unroll
+  for (int blk = 0; blk < NB; ++blk) {
+    const int32_t t = e.tc0 + 16 * blk;
+    pg[blk] = (e.live && e.data && t < e.te)
+                  ? a.block_table[static_cast<int64_t>(e.b) * a.max_pages + (t >> a.ps_log2)]
+                  : 0;
+  }
+}
+
+template <int D, bool FP8, int NB, int SM>
+__device__ __forceinline__ void issue_kv(const DecodeArgs& a, const Entry& e, const int32_t (&pg)[NB],
+                                         Stage<D, FP8, NB, SM>& st, int lane) {
+  constexpr int ROWB = D * (FP8 ? 1 : 2);
+  constexpr int LPB = ROWB / 64;
+  const int c = lane & 15, j = lane >> 4;
+  const int ps_mask = (1 << a.ps_log2) - 1;
+#pragma unroll
+  for (int blk = 0; blk < NB; ++blk) {
+    const int32_t t0 = e.tc0 + 16 * blk;
+    int32_t page = pg[blk];
+    bool page_ok = true;
+    if (a.debug_bounds && t0 < e.te && (page < 0 || page >= a.num_pages)) {
+      page_ok = false;
+      if (lane == 0) atomicOr(a.status + ST_BITS, PA_DEV_BAD_PAGE);
+    }
+    const uint64_t row0 = cache_row(page, e.g, t0 & ps_mask, a.num_kv_heads, a.ps_log2);
+    const bool ok = page_ok && (t0 + c < e.te);
+    const uint64_t off = (row0 + c) * ROWB + 16 * j;
+    const uint8_t* kp = a.k_cache + off;
+    const uint8_t* vp = a.v_cache + off;
+#pragma unroll
+    for (int i = 0; i < LPB; ++i) {
+      st.k[blk][i] = ok ? ld16(kp + 64 * i) : u32x4{0, 0, 0, 0};
+      st.v[blk][i] = ok ? ld16(vp + 64 * i) : u32x4{0, 0, 0, 0};
+    }
+    if constexpr (SM == PA_SCALE_PER_TOKEN_HEAD) {
+      const bool ok4 = page_ok && (t0 + 4 * j < e.te);
+      const uint64_t srow = row0 + 4 * j;
+      const uint64_t vbase = static_cast<uint64_t>(a.num_pages) * a.num_kv_heads << a.ps_log2;
+      st.ks[blk] = ok4 ? *reinterpret_cast<const f32x4*>(a.kv_scales + srow) : f32x4{0, 0, 0, 0};
+      st.vs[blk] = ok4 ? *reinterpret_cast<const f32x4*>(a.kv_scales + vbase + srow)
+                       : f32x4{0, 0, 0, 0};
+    }
+  }
+}
+
+template <int D, bool FP8, int RT>
+__device__ __forceinline__ void load_q(const DecodeArgs& a, const Entry& e, int lane,
+                                       bf16x8 (&qn)[RT * (D / 32)]) {
+  constexpr int KC = D / 32;
+  const int c = lane & 15, j = lane >> 4;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int r = 16 * rt + c;
+    const bool ok = r < a.rows;
+    const int i = ok ? r / a.group : 0;
+    const int h = e.g * a.group + (ok ? r - i * a.group : 0);
+    const uint16_t* qp = a.q + ((static_cast<int64_t>(e.b) * a.q_len + i) * a.num_q_heads + h) * D;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      u32x4 w = ok ? *reinterpret_cast<const u32x4*>(qp + qk_dim<FP8>(kc, j)) : u32x4{0, 0, 0, 0};
+      qn[rt * KC + kc] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+}
+
+template <int D, bool FP8, int SM, int RT, int NB, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void partition_kernel(DecodeArgs a) {
+  using C = Cfg<D, FP8, RT, NB, NW>;
+  constexpr int KC = C::KC, DT = C::DT, TC = C::TC, LPB = C::LPB;
+
+  __shared__ __attribute__((aligned(16))) uint8_t lds_waves[NW * C::WBYTES];
+  __shared__ float st_m[NW][RT * 16];
+  __shared__ float st_l[NW][RT * 16];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15, j = lane >> 4;
+  const int w = blockIdx.x;
+
+  Cursor cur;
+  cur.s = a.wg_seg_begin[w];
+  cur.s_end = a.wg_seg_begin[w + 1];
+  if (cur.s >= cur.s_end) return;
+  cur.live = 1;
+  cursor_load(cur, a, wave);
+
+  // Softmax scale in the exp2 domain; per-tensor scales are folded in here
+  // (K scale into the scores, V scale into the output).
+  float qk_f = a.qk_scale_log2;
+  float out_f = a.out_scale;
+  if constexpr (SM == PA_SCALE_PER_TENSOR) {
+    qk_f *= a.kv_scales[0];
+    out_f = a.kv_scales[1];
+  }
+
+  // Query index of each of this lane's rows (rows past R see every key).
+  int row_q[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int r = 16 * rt + c;
+    row_q[rt] = r < a.rows ? r / a.group : a.q_len;
+  }
+
+  uint8_t* const wlds = lds_waves + wave * C::WBYTES;
+
+  Entry e0 = cursor_take<TC, NW>(cur, a, wave);
+  Entry e1 = cursor_take<TC, NW>(cur, a, wave);
+  Entry e2 = cursor_take<TC, NW>(cur, a, wave);
+
+  bf16x8 q[RT * KC];
+  Stage<D, FP8, NB, SM> sA, sB;
+  int32_t pg[NB];
+
+  // prologue: K/V of entry 0, pages of entry 1
+  load_pages<NB>(a, e0, pg);
+  if (e0.data) issue_kv<D, FP8, NB, SM>(a, e0, pg, sA, lane);
+  load_pages<NB>(a, e1, pg);
+
+  float m[RT], l[RT];
+  f32x4 o[DT][RT];
+
+  auto step = [&](Stage<D, FP8, NB, SM>& cs, Stage<D, FP8, NB, SM>& ns) {
+    if (e0.first) {
+      // Q rows of the new segment's pair (issued before the next chunk's
+      // K/V so waiting for them does not wait for that prefetch)
+      load_q<D, FP8, RT>(a, e0, lane, q);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        m[rt] = neg_inf();
+        l[rt] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt][rt] = f32x4{0, 0, 0, 0};
+      }
+    }
+    // stage 1: K/V of the next chunk; stage 0: block-table pages two chunks ahead
+    if (e1.live && e1.data) issue_kv<D, FP8, NB, SM>(a, e1, pg, ns, lane);
+    load_pages<NB>(a, e2, pg);
+
+    if (e0.data) {
+      // ---- S^T = K Q^T: lane holds tokens 16 blk + 4 j + i of row 16 rt + c
+      f32x4 s[NB][RT];
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) s[blk][rt] = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          bf16x8 kf;
+          if constexpr (FP8) {
+            const u32x4 wv = cs.k[blk][kc >> 1];
+            kf = (kc & 1) ? fp8x8_to_bf16(wv.z, wv.w) : fp8x8_to_bf16(wv.x, wv.y);
+          } else {
+            kf = __builtin_bit_cast(bf16x8, cs.k[blk][kc]);
+          }
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+            s[blk][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, q[rt * KC + kc], s[blk][rt], 0, 0, 0);
+        }
+      }
+
+      // ---- scale, causal mask, online softmax (exp2 domain)
+      const bool full = (e0.tc0 + TC <= e0.te) && (e0.tc0 + TC - 1 <= e0.ctx - a.q_len);
+      constexpr bool per_tok = SM == PA_SCALE_PER_TOKEN_HEAD;
+      float pv[NB][RT][4];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const int lim = min(e0.te - 1, e0.ctx - a.q_len + row_q[rt]);
+        float x[NB][4];
+        float cm = neg_inf();
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float v = s[blk][rt][i] * qk_f;
+            if constexpr (per_tok) v *= cs.ks[blk][i];
+            if (!full) v = (e0.tc0 + 16 * blk + 4 * j + i <= lim) ? v : neg_inf();
+            x[blk][i] = v;
+            cm = fmaxf(cm, v);
+          }
+        }
+        cm = fmaxf(cm, __shfl_xor(cm, 16));
+        cm = fmaxf(cm, __shfl_xor(cm, 32));
+        const float mn = fmaxf(m[rt], cm);
+        const float mu = mn == neg_inf() ? 0.f : mn;
+        const float alpha = __builtin_amdgcn_exp2f(m[rt] - mu);
+        float ps = 0.f;
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float p = __builtin_amdgcn_exp2f(x[blk][i] - mu);
+            ps += p;
+            float q2 = p;
+            if constexpr (per_tok) {
+              q2 = p * cs.vs[blk][i];
+              if (!full) q2 = (e0.tc0 + 16 * blk + 4 * j + i <= lim) ? q2 : 0.f;
+            }
+            pv[blk][rt][i] = q2;
+          }
+        }
+        l[rt] = l[rt] * alpha + ps;
+        m[rt] = mn;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt][rt] *= alpha;
+      }
+
+      // ---- V rows -> wave-private LDS tile (row-major bf16)
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk) {
+        uint8_t* vrow = wlds + (16 * blk + c) * C::VROW;
+#pragma unroll
+        for (int i = 0; i < LPB; ++i) {
+          const u32x4 wv = cs.v[blk][i];
+          if constexpr (FP8) {
+            const bf16x8 lo = fp8x8_to_bf16(wv.x, wv.y);
+            const bf16x8 hi = fp8x8_to_bf16(wv.z, wv.w);
+            const u32x4 l4 = __builtin_bit_cast(u32x4, lo);
+            const u32x4 h4 = __builtin_bit_cast(u32x4, hi);
+            uint8_t* dst = vrow + 128 * i + 32 * j;
+            *reinterpret_cast<u32x2*>(dst + 0) = u32x2{l4.x, l4.y};
+            *reinterpret_cast<u32x2*>(dst + 8) = u32x2{l4.z, l4.w};
+            *reinterpret_cast<u32x2*>(dst + 16) = u32x2{h4.x, h4.y};
+            *reinterpret_cast<u32x2*>(dst + 24) = u32x2{h4.z, h4.w};
+          } else {
+            uint8_t* dst = vrow + 64 * i + 16 * j;
+            *reinterpret_cast<u32x2*>(dst + 0) = u32x2{wv.x, wv.y};
+            *reinterpret_cast<u32x2*>(dst + 8) = u32x2{wv.z, wv.w};
+          }
+        }
+      }
+
+      // ---- O^T += V^T P^T (token order inside a k-step is the S^T lane order)
+      const uint16_t* vt = reinterpret_cast<const uint16_t*>(wlds) + (4 * j) * (C::VROW / 2) + c;
+      if constexpr (NB == 1) {
+        bf16x4 bp[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const f32x4 f = {pv[0][rt][0], pv[0][rt][1], pv[0][rt][2], pv[0][rt][3]};
+          bp[rt] = __builtin_convertvector(f, bf16x4);
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          uint16_t av[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) av[i] = vt[i * (C::VROW / 2) + 16 * dt];
+          const bf16x4 A = __builtin_bit_cast(bf16x4, av);
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+            o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, bp[rt], o[dt][rt], 0, 0, 0);
+        }
+      } else {
+        bf16x8 bp[NB / 2][RT];
+#pragma unroll
+        for (int qq = 0; qq < NB / 2; ++qq) {
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            const f32x8 f = {pv[2 * qq][rt][0], pv[2 * qq][rt][1], pv[2 * qq][rt][2], pv[2 * qq][rt][3],
+                             pv[2 * qq + 1][rt][0], pv[2 * qq + 1][rt][1], pv[2 * qq + 1][rt][2],
+                             pv[2 * qq + 1][rt][3]};
+            bp[qq][rt] = __builtin_convertvector(f, bf16x8);
+          }
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+          for (int qq = 0; qq < NB / 2; ++qq) {
+            uint16_t av[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              av[i] = vt[(32 * qq + i) * (C::VROW / 2) + 16 * dt];
+              av[4 + i] = vt[(32 * qq + 16 + i) * (C::VROW / 2) + 16 * dt];
+            }
+            const bf16x8 A = __builtin_bit_cast(bf16x8, av);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+              o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, bp[qq][rt], o[dt][rt], 0, 0, 0);
+          }
+        }
+      }
+    }
+
+    if (e0.last) {
+      // ---- merge the NW waves' (max, sum, O) of this segment
+      float lt[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        float v = l[rt];
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        lt[rt] = v;
+        if (j == 0) {
+          st_m[wave][16 * rt + c] = m[rt];
+          st_l[wave][16 * rt + c] = v;
+        }
+      }
+      __syncthreads();
+      const int pair_rows = a.rows;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        float M = neg_inf();
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, st_m[ww][16 * rt + c]);
+        const float Mu = M == neg_inf() ? 0.f : M;
+        const float f = __builtin_amdgcn_exp2f(m[rt] - Mu);
+        float* ob = reinterpret_cast<float*>(wlds);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          *reinterpret_cast<f32x4*>(ob + c * C::OROW + 16 * dt + 4 * j) = o[dt][rt] * f;
+        __syncthreads();
+        for (int u = threadIdx.x; u < 16 * (D / 8); u += C::THREADS) {
+          const int row = u / (D / 8);
+          const int d0 = (u - row * (D / 8)) * 8;
+          const int r = 16 * rt + row;
+          if (r < pair_rows) {
+            float Mr = neg_inf();
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) Mr = fmaxf(Mr, st_m[ww][16 * rt + row]);
+            const float Mru = Mr == neg_inf() ? 0.f : Mr;
+            float L = 0.f;
+            f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) {
+              L += st_l[ww][16 * rt + row] * __builtin_amdgcn_exp2f(st_m[ww][16 * rt + row] - Mru);
+              const float* src = reinterpret_cast<const float*>(lds_waves + ww * C::WBYTES) +
+                                 row * C::OROW + d0;
+              acc0 += *reinterpret_cast<const f32x4*>(src);
+              acc1 += *reinterpret_cast<const f32x4*>(src + 4);
+            }
+            const float inv = L > 0.f ? out_f / L : 0.f;
+            acc0 *= inv;
+            acc1 *= inv;
+            if (e0.slot < 0) {
+              const int qi = r / a.group;
+              const int h = e0.g * a.group + (r - qi * a.group);
+              const f32x8 f8 = {acc0.x, acc0.y, acc0.z, acc0.w, acc1.x, acc1.y, acc1.z, acc1.w};
+              const bf16x8 ob8 = __builtin_convertvector(f8, bf16x8);
+              *reinterpret_cast<bf16x8*>(a.out + ((static_cast<int64_t>(e0.b) * a.q_len + qi) *
+                                                      a.num_q_heads + h) * D + d0) = ob8;
+            } else {
+              float* dst = a.partial_o + (static_cast<int64_t>(e0.slot) * pair_rows + r) * D + d0;
+              *reinterpret_cast<f32x4*>(dst) = acc0;
+              *reinterpret_cast<f32x4*>(dst + 4) = acc1;
+              if (d0 == 0)
+                a.partial_lse[static_cast<int64_t>(e0.slot) * pair_rows + r] =
+                    L > 0.f ? (Mru + __log2f(L)) * kLn2 : neg_inf();
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+
+    e0 = e1;
+    e1 = e2;
+    e2 = cursor_take<TC, NW>(cur, a, wave);
+  };
+
+  for (;;) {
+    step(sA, sB);
+    if (!e0.live) break;
+    step(sB, sA);
+    if (!e0.live) break;
+  }
+}
+
+// One workgroup per (sequence, kv head) pair; pairs with a single segment
+// were finished by the partition pass.
+constexpr int kReduceThreads = 256;
+
+template <int D>
+__global__ __launch_bounds__(kReduceThreads) void reduce_kernel(DecodeArgs a) {
+  const int p = blockIdx.x;
+  const int n = a.nseg[p];
+  if (n <= 1) return;
+  const int base = a.seg_base[p];
+  const int b = p / a.num_kv_heads;
+  const int g = p - b * a.num_kv_heads;
+  const int R = a.rows;
+  for (int u = threadIdx.x; u < R * (D / 8); u += kReduceThreads) {
+    const int r = u / (D / 8);
+    const int d0 = (u - r * (D / 8)) * 8;
+    float M = neg_inf();
+    for (int s = 0; s < n; ++s) M = fmaxf(M, a.partial_lse[static_cast<int64_t>(base + s) * R + r]);
+    const float Mu = M == neg_inf() ? 0.f : M;
+    float W = 0.f;
+    f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+    for (int s = 0; s < n; ++s) {
+      const int64_t row = static_cast<int64_t>(base + s) * R + r;
+      const float wgt = __builtin_amdgcn_exp2f((a.partial_lse[row] - Mu) * kLog2e);
+      W += wgt;
+      const float* src = a.partial_o + row * D + d0;
+      acc0 += wgt * *reinterpret_cast<const f32x4*>(src);
+      acc1 += wgt * *reinterpret_cast<const f32x4*>(src + 4);
+    }
+    const float inv = W > 0.f ? 1.f / W : 0.f;
+    acc0 *= inv;
+    acc1 *= inv;
+    const int qi = r / a.group;
+    const int h = g * a.group + (r - qi * a.group);
+    const f32x8 f8 = {acc0.x, acc0.y, acc0.z, acc0.w, acc1.x, acc1.y, acc1.z, acc1.w};
+    *reinterpret_cast<bf16x8*>(a.out + ((static_cast<int64_t>(b) * a.q_len + qi) * a.num_q_heads + h) *
+                                           D + d0) = __builtin_convertvector(f8, bf16x8);
+  }
+}
+
+// Debug gather: rows of every (pair, token < ctx) through the block table,
+// with the partition pass's cache_row() addressing.
+__global__ __launch_bounds__(64) void gather_kernel(DecodeArgs a, int row_bytes, int capacity,
+                                                    uint8_t* k_out, uint8_t* v_out) {
+  const int p = blockIdx.x;
+  const int t = blockIdx.y * 64 + threadIdx.x;
+  const int b = p / a.num_kv_heads;
+  const int g = p - b * a.num_kv_heads;
+  if (t >= a.context_lens[b] || t >= capacity) return;
+  const int32_t page = a.block_table[static_cast<int64_t>(b) * a.max_pages + (t >> a.ps_log2)];
+  if (a.debug_bounds && (page < 0 || page >= a.num_pages)) {
+    atomicOr(a.status + ST_BITS, PA_DEV_BAD_PAGE);
+    return;
+  }
+  const uint64_t src = cache_row(page, g, t & ((1 << a.ps_log2) - 1), a.num_kv_heads, a.ps_log2) * row_bytes;
+  const uint64_t dst = (static_cast<uint64_t>(p) * capacity + t) * row_bytes;
+  for (int x = 0; x < row_bytes; x += 16) {
+    *reinterpret_cast<u32x4*>(k_out + dst + x) = ld16(a.k_cache + src + x);
+    *reinterpret_cast<u32x4*>(v_out + dst + x) = ld16(a.v_cache + src + x);
+  }
+}
+
+template <int D, bool FP8, int SM, int RT, int NB, int NW>
+hipError_t launch_partition_t(const DecodeArgs& a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((partition_kernel<D, FP8, SM, RT, NB, NW>), dim3(grid), dim3(NW * 64), 0, s, a);
+  return hipGetLastError();
+}
+
+using LaunchFn = hipError_t (*)(const DecodeArgs&, int, hipStream_t);
+
+struct VariantEntry {
+  Variant v;
+  LaunchFn fn;
+};
+
+#define PA_V(D, F, SM, RT, NB, NW) \
+  { {D, F, SM, RT, NB, NW}, launch_partition_t<D, F != 0, SM, RT, NB, NW> }
+const VariantEntry kVariants[] = {
+    PA_V(128, 0, 0, 1, 2, 4), PA_V(128, 0, 0, 2, 2, 4), PA_V(128, 0, 0, 4, 2, 4),
+    PA_V(256, 0, 0, 1, 1, 4), PA_V(256, 0, 0, 2, 1, 4),
+    PA_V(128, 1, 1, 1, 2, 4), PA_V(128, 1, 1, 2, 2, 4), PA_V(128, 1, 1, 4, 2, 4),
+    PA_V(128, 1, 2, 1, 2, 4), PA_V(128, 1, 2, 2, 2, 4), PA_V(128, 1, 2, 4, 2, 4),
+    PA_V(256, 1, 1, 1, 1, 4), PA_V(256, 1, 1, 2, 1, 4),
+    PA_V(256, 1, 2, 1, 1, 4), PA_V(256, 1, 2, 2, 1, 4),
+};
+#undef PA_V
+
+}  // namespace
+
+int num_variants() { return static_cast<int>(sizeof(kVariants) / sizeof(kVariants[0])); }
+
+const Variant& variant(int i) { return kVariants[i].v; }
+
+int pick_variant(int head_dim, int fp8, int scale_mode, int rows) {
+  const int rt = (rows + 15) / 16;
+  int best = -1;
+  for (int i = 0; i < num_variants(); ++i) {
+    const Variant& v = kVariants[i].v;
+    if (v.head_dim != head_dim || v.fp8 != fp8 || v.scale_mode != scale_mode || v.row_tiles < rt)
+      continue;
+    if (best < 0 || v.row_tiles < kVariants[best].v.row_tiles) best = i;
+  }
+  return best;
+}
+
+hipError_t launch_partition(int vi, const DecodeArgs& a, int grid, hipStream_t s) {
+  return kVariants[vi].fn(a, grid, s);
+}
+
+hipError_t launch_reduce(const DecodeArgs& a, int head_dim, int num_pairs, hipStream_t s) {
+  if (head_dim == 128)
+    hipLaunchKernelGGL(reduce_kernel<128>, dim3(num_pairs), dim3(kReduceThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(reduce_kernel<256>, dim3(num_pairs), dim3(kReduceThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const DecodeArgs& a, int head_dim, int elt_bytes, int capacity,
+                         uint8_t* k_out, uint8_t* v_out, hipStream_t s) {
+  const int pairs = a.batch * a.num_kv_heads;
+  hipLaunchKernelGGL(gather_kernel, dim3(pairs, (capacity + 63) / 64), dim3(64), 0, s, a,
+                     head_dim * elt_bytes, capacity, k_out, v_out);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,132 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol include/pa.h
+declares, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_attention_decode_block_amd as pa
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "pa.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = pa.lib()
+    names = _declared()
+    assert "pa_decode" in names and "pa_plan" in names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_struct_sizes_match_header():
+    # 13 int32 dims; the plan is 4-byte fields up to the pointers, then 8-byte ones
+    assert ctypes.sizeof(pa.pa_dims) == 13 * 4
+    assert ctypes.sizeof(pa.pa_plan_t) % 8 == 0
+    assert pa.pa_plan_t.workspace.offset % 8 == 0
+
+
+def _dims(**kw):
+    base = dict(batch=2, q_len=1, num_q_heads=16, num_kv_heads=1, head_dim=128, page_size=16,
+                num_pages=64, max_pages_per_seq=8)
+    base.update(kw)
+    return pa.make_dims(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), pa.PA_ERR_DIMS),
+    (dict(q_len=0), pa.PA_ERR_DIMS),
+    (dict(num_q_heads=12, num_kv_heads=8), pa.PA_ERR_DIMS),
+    (dict(num_pages=0), pa.PA_ERR_DIMS),
+    (dict(grid_multiplier=17), pa.PA_ERR_DIMS),
+    (dict(flags=4), pa.PA_ERR_DIMS),
+    (dict(head_dim=64), pa.PA_ERR_UNSUPPORTED),
+    (dict(head_dim=96), pa.PA_ERR_UNSUPPORTED),
+    (dict(page_size=8), pa.PA_ERR_UNSUPPORTED),
+    (dict(page_size=48), pa.PA_ERR_UNSUPPORTED),
+    (dict(page_size=2048), pa.PA_ERR_UNSUPPORTED),
+    (dict(partition_size=24), pa.PA_ERR_UNSUPPORTED),
+    (dict(kv_dtype=2), pa.PA_ERR_UNSUPPORTED),
+    (dict(kv_scale_mode=pa.PA_SCALE_PER_TENSOR), pa.PA_ERR_SCALE_MODE),
+    (dict(kv_dtype=pa.PA_KV_FP8_E4M3FN), pa.PA_ERR_SCALE_MODE),
+    (dict(q_len=5, num_q_heads=16, num_kv_heads=1), pa.PA_ERR_UNSUPPORTED),      # 80 rows
+    (dict(head_dim=256, q_len=3, num_q_heads=16, num_kv_heads=1), pa.PA_ERR_UNSUPPORTED),
+])
+def test_dims_rejected_on_host(kw, code):
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_workspace_bytes(_dims(**kw), 256)
+    assert e.value.code == code, e.value.text
+    assert pa.pa_last_error()
+    # pa_plan validates the same way before touching a device
+    c = pa.pa_plan_t()
+    rc = pa.lib().pa_plan(ctypes.byref(_dims(**kw)), 0x1000, 0x100000, 1 << 30, ctypes.byref(c), None)
+    assert rc == code
+
+
+def test_workspace_size_grows_with_work():
+    small = pa.pa_workspace_bytes(_dims(), 256)
+    big = pa.pa_workspace_bytes(_dims(batch=64, max_pages_per_seq=512), 256)
+    assert 0 < small < big
+    assert pa.pa_workspace_bytes(_dims(), 80) < small
+
+
+def test_plan_argument_errors():
+    L = pa.lib()
+    c = pa.pa_plan_t()
+    d = _dims()
+    assert L.pa_plan(ctypes.byref(d), None, 0x100000, 1 << 30, ctypes.byref(c), None) == pa.PA_ERR_NULL
+    assert L.pa_plan(ctypes.byref(d), 0x1000, None, 1 << 30, ctypes.byref(c), None) == pa.PA_ERR_WORKSPACE
+    assert L.pa_plan(ctypes.byref(d), 0x1000, 0x100010, 1 << 30, ctypes.byref(c), None) == pa.PA_ERR_ALIGN
+    assert L.pa_plan(ctypes.byref(d), 0x1002, 0x100000, 1 << 30, ctypes.byref(c), None) == pa.PA_ERR_ALIGN
+
+
+def _fake_plan(**kw):
+    c = pa.pa_plan_t()
+    c.magic = pa.PA_PLAN_MAGIC
+    c.dims = _dims(**kw)
+    return c
+
+
+def _decode(c, q=0x10000, k=0x20000, v=0x30000, bt=0x40000, ctx=0x50000, q_len=1,
+            mode=pa.PA_SCALE_NONE, scales=None, out=0x60000):
+    return pa.lib().pa_decode(ctypes.byref(c) if c is not None else None, q, k, v, bt, ctx, q_len,
+                              0.1, mode, scales, out, None)
+
+
+def test_decode_argument_errors_before_any_device_call():
+    c = _fake_plan()
+    assert _decode(None) == pa.PA_ERR_NULL
+    assert _decode(c, q=None) == pa.PA_ERR_NULL
+    assert _decode(c, out=None) == pa.PA_ERR_NULL
+    unbuilt = pa.pa_plan_t()
+    assert _decode(unbuilt) == pa.PA_ERR_PLAN_MISMATCH
+    assert _decode(c, q=0x10008) == pa.PA_ERR_ALIGN
+    assert _decode(c, k=0x20004) == pa.PA_ERR_ALIGN
+    assert _decode(c, out=0x60002) == pa.PA_ERR_ALIGN
+    assert _decode(c, bt=0x40002) == pa.PA_ERR_ALIGN
+    assert _decode(c, q_len=2) == pa.PA_ERR_PLAN_MISMATCH
+    assert _decode(c, mode=pa.PA_SCALE_PER_TENSOR, scales=0x70000) == pa.PA_ERR_PLAN_MISMATCH
+    assert _decode(c, scales=0x70000) == pa.PA_ERR_SCALE_MODE
+    f8 = _fake_plan(kv_dtype=pa.PA_KV_FP8_E4M3FN, kv_scale_mode=pa.PA_SCALE_PER_TOKEN_HEAD)
+    assert _decode(f8, mode=pa.PA_SCALE_PER_TOKEN_HEAD) == pa.PA_ERR_SCALE_MODE
+    assert _decode(f8, mode=pa.PA_SCALE_PER_TOKEN_HEAD, scales=0x70008) == pa.PA_ERR_ALIGN
+    L = pa.lib()
+    assert L.pa_decode_reduce(ctypes.byref(c), 2, 0, 0x60000, None) == pa.PA_ERR_PLAN_MISMATCH
+    assert L.pa_decode_reduce(ctypes.byref(c), 1, 0, None, None) == pa.PA_ERR_NULL
+    st = ctypes.c_int32()
+    assert L.pa_plan_status(None, ctypes.byref(st), None) == pa.PA_ERR_NULL
+    assert L.pa_debug_gather(ctypes.byref(c), 0x20000, 0x30000, 0x40000, 0x50000, None, 0x80000,
+                             None) == pa.PA_ERR_NULL
+
+
+def test_status_strings():
+    for code in range(-9, 1):
+        s = pa.pa_status_string(code)
+        assert s and s != "unknown status"
+    assert pa.pa_status_string(-100) == "unknown status"

@@ -1,0 +1,111 @@
+"""Decode parity: the HIP path vs the CPU oracle, element by element.
+
+Tolerance |gpu - oracle| <= tol + tol * |oracle| with tol = 8e-3 for bf16 KV
+and 2e-2 for fp8 KV (the oracle decodes the same fp8 bytes). Inputs are the
+seeded workloads (unused pages and dead slots poisoned with NaN), at sizes
+the float64 oracle finishes in seconds but that still span several pages,
+partitions and a ragged tail.
+"""
+import pytest
+import torch
+
+import paged_attention_decode_block_amd as pa
+import workloads as W
+from tests.gpu_util import check, run, say
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    # the two same-shape cases of the Ascend issue, full size
+    "C1": W.C1,
+    "C2": W.C2,
+    # reduced versions of the batched / fp8 / long-context workloads
+    "C3r": W.scaled(W.C3, batch=6, ctx_lo=1, ctx_hi=900, max_ctx=1024),
+    "C4r_q1_tok": W.scaled(W.C4_Q1_TOK, batch=3, ctx_lo=1, ctx_hi=2500, max_ctx=3072),
+    "C4r_q4_tok": W.scaled(W.C4_Q4_TOK, batch=3, ctx_lo=4, ctx_hi=2500, max_ctx=3072),
+    "C4r_q1_ten": W.scaled(W.C4_Q1_TEN, batch=3, ctx_lo=1, ctx_hi=2500, max_ctx=3072),
+    "C4r_q4_ten": W.scaled(W.C4_Q4_TEN, batch=3, ctx_lo=4, ctx_hi=2500, max_ctx=3072),
+    "C5r": W.scaled(W.C5, batch=2, ctx_lo=8, ctx_hi=1500, max_ctx=2048, pool_slack=0.1),
+}
+
+
+@pytest.mark.parametrize("seed", W.SEEDS)
+@pytest.mark.parametrize("name", list(SMALL))
+def test_decode_parity(name, seed):
+    w = W.generate(SMALL[name], seed)
+    say(f"[decode] {name} seed={seed} ctx={w.context_lens.tolist()}")
+    out, plan = run(w)
+    err = check(w, out, f"{name}/{seed}")
+    assert pa.pa_plan_status(plan) == 0
+    say(f"[decode] {name} seed={seed} max abs err {err:.3e}")
+
+
+@pytest.mark.parametrize("P", [16, 32, 64, 4096])
+def test_partition_sizes(P):
+    # P = 16 with many sequences gives more items than workgroups, so segments
+    # span several items and pairs split over several workgroups
+    spec = W.scaled(W.C3, batch=12, ctx_lo=100, ctx_hi=1500, max_ctx=2048)
+    w = W.generate(spec, 2039)
+    say(f"[decode] partition {P}")
+    out, _ = run(w, partition=P)
+    check(w, out, f"P={P}")
+
+
+@pytest.mark.parametrize("mult", [1, 2, 4])
+def test_grid_multiplier(mult):
+    spec = W.scaled(W.C4_Q4_TOK, batch=4, ctx_lo=3000, ctx_hi=9000, max_ctx=9216)
+    w = W.generate(spec, 2026)
+    say(f"[decode] grid multiplier {mult}")
+    out, plan = run(w, grid_multiplier=mult)
+    assert plan.c.grid == plan.c.num_cus * mult
+    check(w, out, f"mult={mult}")
+
+
+@pytest.mark.parametrize("ps", [16, 32, 64, 128, 256, 512, 1024])
+def test_page_sizes(ps):
+    spec = W.scaled(W.C3, batch=3, ctx_lo=1, ctx_hi=1100, page_size=ps, max_ctx=2048)
+    w = W.generate(spec, 2029)
+    say(f"[decode] page size {ps}")
+    out, _ = run(w)
+    check(w, out, f"ps={ps}")
+
+
+@pytest.mark.parametrize("q_len,hq,hkv,d", [(1, 8, 8, 128), (2, 8, 2, 128), (3, 16, 1, 128),
+                                            (1, 32, 1, 128), (2, 32, 1, 128), (4, 12, 1, 128),
+                                            (8, 4, 4, 256), (2, 16, 2, 256), (4, 8, 1, 256),
+                                            (3, 10, 1, 256)])
+def test_row_shapes(q_len, hq, hkv, d):
+    # rows per kv head R = q_len * hq / hkv from 1 to 64: one to four 16-row tiles
+    spec = W.Spec(f"rows_{q_len}x{hq}/{hkv}_d{d}", 3, q_len, hq, hkv, d, 32, q_len, 700,
+                  max_ctx=1024)
+    w = W.generate(spec, 2026)
+    say(f"[decode] {spec.name} ctx={w.context_lens.tolist()}")
+    out, _ = run(w)
+    check(w, out, spec.name)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8_tok", "fp8_ten"])
+def test_edge_contexts(kv):
+    base = {"bf16": W.scaled(W.C5, batch=6, q_len=4, num_q_heads=8, num_kv_heads=2, head_dim=128),
+            "fp8_tok": W.scaled(W.C4_Q4_TOK, batch=6),
+            "fp8_ten": W.scaled(W.C4_Q4_TEN, batch=6)}[kv]
+    ps = base.page_size
+    # minimum (ctx = q_len), a single page, a page + 1, a partition + 1, a
+    # multiple of the partition, and the block-table capacity
+    cap = -(-max(600, ps + 1) // ps) * ps
+    ctxs = [4, ps, ps + 1, 257, 512, cap]
+    spec = W.scaled(base, batch=len(ctxs), ctx_lo=min(ctxs), ctx_hi=max(ctxs), max_ctx=cap,
+                    pool_slack=0.5)
+    w = W.generate(spec, 2026, context_lens=ctxs)
+    say(f"[decode] edges {kv} ctx={ctxs}")
+    out, plan = run(w)
+    check(w, out, f"edges/{kv}")
+    assert pa.pa_plan_status(plan) == 0
+
+
+def test_bad_context_reports_and_writes_nothing():
+    spec = W.scaled(W.C3, batch=2, ctx_lo=30, ctx_hi=40, max_ctx=64)
+    w = W.generate(spec, 2026)
+    w.context_lens[1] = 65                          # past capacity
+    out, plan = run(w)
+    assert pa.pa_plan_status(plan) == pa.PA_DEV_BAD_CONTEXT

@@ -53,6 +53,18 @@ def _check(pl, ctxs, Hkv, P, G):
             used.setdefault(slot, set()).add((p, w))
     assert sorted(used) == list(range(total))
     assert all(len(v) == 1 for v in used.values())
+    # segments: one per (workgroup, pair) run, tokens contiguous, slots as items
+    assert len(pl.segs) == sum(pl.nseg) == pl.pseg_base[-1]
+    assert pl.wg_seg_begin[0] == 0 and pl.wg_seg_begin[-1] == len(pl.segs)
+    for w in range(G):
+        runs = []
+        for x in range(wb[w], wb[w + 1]):
+            p, t0, t1, slot = pl.items[x]
+            if runs and runs[-1][0] == p:
+                runs[-1][2] = t1
+            else:
+                runs.append([p, t0, t1, slot])
+        assert [list(s) for s in pl.segs[pl.wg_seg_begin[w]:pl.wg_seg_begin[w + 1]]] == runs
 
 
 @pytest.mark.parametrize("seed", range(40))

@@ -200,15 +200,19 @@ def pool_size(spec: Spec, pages_needed: int) -> int:
     return int(math.ceil((1.0 + spec.pool_slack) * pages_needed - 1e-9))
 
 
+def draw_context_lens(spec: Spec, seed: int) -> np.ndarray:
+    """The context lengths of (spec, seed) alone (stream [seed, 0])."""
+    if spec.ctx_lo == spec.ctx_hi:
+        return np.full(spec.batch, spec.ctx_lo, dtype=np.int64)
+    return _rng(seed, 0).integers(spec.ctx_lo, spec.ctx_hi + 1, size=spec.batch, dtype=np.int64)
+
+
 def generate(spec: Spec, seed: int, poison: bool = True,
              context_lens: Optional[list] = None) -> Workload:
     """Draw one workload on the host. ``context_lens`` overrides the drawn lengths."""
     B, ps, D, Hkv = spec.batch, spec.page_size, spec.head_dim, spec.num_kv_heads
     if context_lens is None:
-        if spec.ctx_lo == spec.ctx_hi:
-            ctx = np.full(B, spec.ctx_lo, dtype=np.int64)
-        else:
-            ctx = _rng(seed, 0).integers(spec.ctx_lo, spec.ctx_hi + 1, size=B, dtype=np.int64)
+        ctx = draw_context_lens(spec, seed)
     else:
         ctx = np.asarray(context_lens, dtype=np.int64)
         assert ctx.shape == (B,)
