@@ -20,6 +20,10 @@ must reproduce it bit for bit:
              earlier pairs p' with nseg[p'] > 1
   slot       of an item: -1 for a pair with nseg = 1, else seg_base[p] + the
              index of its segment among the pair's segments, in item order
+  segs       one (pair, tok_begin, tok_end, slot) per segment, in workgroup
+             order; wg_seg_begin[w] = index of workgroup w's first segment
+  pseg_base  exclusive prefix sum of nseg over all pairs
+  batch_base index of the first item of sequence b (B + 1 entries)
   status     1 if some ctx_b is outside [max(1, q_len), max_pages * page_size];
              then the plan is empty (N = 0, every range empty, nseg = 0)
 
@@ -43,6 +47,10 @@ class Plan:
     nseg: List[int]             # per pair
     seg_base: List[int]         # per pair + 1 (last = total slots)
     status: int
+    segs: List[tuple] = dataclasses.field(default_factory=list)
+    wg_seg_begin: List[int] = dataclasses.field(default_factory=list)
+    pseg_base: List[int] = dataclasses.field(default_factory=list)
+    batch_base: List[int] = dataclasses.field(default_factory=list)
 
 
 def plan(context_lens, num_kv_heads: int, partition: int, grid: int, q_len: int,
@@ -52,7 +60,8 @@ def plan(context_lens, num_kv_heads: int, partition: int, grid: int, q_len: int,
     pairs = B * num_kv_heads
     cap = max_pages_per_seq * page_size
     if any(c < max(1, q_len) or c > cap for c in ctxs):
-        return Plan(0, [], [0] * (grid + 1), [0] * pairs, [0] * (pairs + 1), STATUS_BAD_CONTEXT)
+        return Plan(0, [], [0] * (grid + 1), [0] * pairs, [0] * (pairs + 1), STATUS_BAD_CONTEXT,
+                    [], [0] * (grid + 1), [0] * (pairs + 1), [0] * (B + 1))
 
     raw = []
     for b, c in enumerate(ctxs):
@@ -86,4 +95,24 @@ def plan(context_lens, num_kv_heads: int, partition: int, grid: int, q_len: int,
         _, j = seg_of_item[x]
         slot = -1 if nseg[p] == 1 else seg_base[p] + j
         items.append((p, t0, t1, slot))
-    return Plan(N, items, wg_begin, nseg, seg_base, STATUS_OK)
+
+    # Segments in workgroup order, each spanning its run of items.
+    segs = []
+    wg_seg_begin = []
+    for w in range(grid):
+        wg_seg_begin.append(len(segs))
+        for x in range(wg_begin[w], wg_begin[w + 1]):
+            p, t0, t1, slot = items[x]
+            if x == wg_begin[w] or items[x - 1][0] != p:
+                segs.append([p, t0, t1, slot])
+            else:
+                segs[-1][2] = t1
+    wg_seg_begin.append(len(segs))
+    pseg_base = [0] * (pairs + 1)
+    for p in range(pairs):
+        pseg_base[p + 1] = pseg_base[p] + nseg[p]
+    batch_base = [0]
+    for c in ctxs:
+        batch_base.append(batch_base[-1] + num_kv_heads * -(-c // partition))
+    return Plan(N, items, wg_begin, nseg, seg_base, STATUS_OK, [tuple(x) for x in segs],
+                wg_seg_begin, pseg_base, batch_base)
