@@ -1,0 +1,263 @@
+#!/usr/bin/env python3
+"""Paged-attention decode benchmark on one MI355X.
+
+One step = one pass of the whole hot path over one batch: pa_plan (work
+list), the persistent partition kernel and the log-sum-exp reduce. Inputs are
+seeded synthetic workloads (workloads.CONFIGS) already resident in HBM; before
+every step a 1 GiB fill evicts L2 and the 256 MB Infinity Cache, outside the
+timed events, so KV really streams from HBM. HIP events on the launch stream
+bracket the plan, the partition kernel and the reduce of every step (the
+method of Ascend/RecSDK issue #1281, section "测试方法": warmups, then
+samples, median).
+
+The JSON line's `value` is KV-read GB/s of the whole step on the headline
+workload (batched GQA decode); `per_config` carries every workload; `roofline`
+is the partition kernel's algorithmic KV bytes over its mean event duration
+against 8 TB/s; `cpu_baseline` times the CPU oracle on a bounded sample of the
+headline workload, whose outputs also check the GPU's.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged-attn decode latency (µs) and KV-read HBM GB/s (% of peak), 1 GPU"
+HBM_PEAK_GBS = 8000.0
+HEADLINE = "C3_batched_gqa"
+FLUSH_BYTES = 1 << 30
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=51)
+    p.add_argument("--warmup", type=int, default=16)
+    p.add_argument("--seed", type=int, default=2026)
+    p.add_argument("--only", default="", help="comma list of workloads (default: all)")
+    p.add_argument("--grid-multiplier", type=int, default=0)
+    p.add_argument("--partition", type=int, default=0)
+    p.add_argument("--no-flush", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="target CPU time of the oracle sample")
+    return p.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build runs the decode on a single MI355X "
+              f"and has no multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_attention_decode_block_amd as pa
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    names = [n for n in W.CONFIGS] if not args.only else args.only.split(",")
+    if HEADLINE not in names and not args.only:
+        names.insert(0, HEADLINE)
+    flush = None if args.no_flush else torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    cus = pa.pa_query_device(0)
+    results = {}
+    keep = {}
+    for name in names:
+        spec = W.CONFIGS[name]
+        t0 = time.time()
+        w = W.generate(spec, args.seed)
+        log(f"{name}: drew inputs in {time.time() - t0:.1f}s, ctx sum {int(w.context_lens.sum())}")
+        d = {k: getattr(w, k).to(dev) for k in ("q", "k_cache", "v_cache", "block_table",
+                                                 "context_lens")}
+        d["kv_scales"] = None if w.kv_scales is None else w.kv_scales.to(dev)
+        kvd = pa.PA_KV_FP8_E4M3FN if spec.kv_dtype == W.KV_FP8 else pa.PA_KV_BF16
+        mode = {W.SCALE_NONE: pa.PA_SCALE_NONE, W.SCALE_PER_TENSOR: pa.PA_SCALE_PER_TENSOR,
+                W.SCALE_PER_TOKEN_HEAD: pa.PA_SCALE_PER_TOKEN_HEAD}[spec.kv_scale_mode]
+        dims = pa.make_dims(batch=spec.batch, q_len=spec.q_len, num_q_heads=spec.num_q_heads,
+                            num_kv_heads=spec.num_kv_heads, head_dim=spec.head_dim,
+                            page_size=spec.page_size, num_pages=w.num_pages,
+                            max_pages_per_seq=spec.max_pages_per_seq, kv_dtype=kvd,
+                            kv_scale_mode=mode,
+                            partition_size=args.partition or spec.partition_size,
+                            grid_multiplier=args.grid_multiplier)
+        ws = torch.empty(pa.pa_workspace_bytes(dims, cus), dtype=torch.uint8, device=dev)
+        out = torch.empty_like(d["q"])
+        stream = torch.cuda.current_stream()
+
+        def step(evs=None):
+            if evs:
+                evs[0].record(stream)
+            plan = pa.pa_plan(dims, d["context_lens"], workspace=ws, stream=stream)
+            if evs:
+                evs[1].record(stream)
+            pa.pa_decode_partition(plan, d["q"], d["k_cache"], d["v_cache"], d["block_table"],
+                                   d["context_lens"], spec.q_len, spec.scale, mode,
+                                   d["kv_scales"], out, stream=stream)
+            if evs:
+                evs[2].record(stream)
+            pa.pa_decode_reduce(plan, spec.q_len, mode, out, stream=stream)
+            if evs:
+                evs[3].record(stream)
+            return plan
+
+        for _ in range(args.warmup):
+            if flush is not None:
+                flush.zero_()
+            step()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t_wall = time.perf_counter()
+        for i in range(args.steps):
+            if flush is not None:
+                flush.zero_()
+            plan = step(evs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_wall
+        status = pa.pa_plan_status(plan)
+        assert status == 0, f"{name}: device status {status}"
+        plan_us = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]
+        part_us = [e[1].elapsed_time(e[2]) * 1e3 for e in evs]
+        red_us = [e[2].elapsed_time(e[3]) * 1e3 for e in evs]
+        step_us = [e[0].elapsed_time(e[3]) * 1e3 for e in evs]
+        dec_us = [e[1].elapsed_time(e[3]) * 1e3 for e in evs]
+        kvb = w.kv_bytes()
+        med = statistics.median
+        r = {
+            "kv_bytes": kvb,
+            "step_us": med(step_us), "decode_us": med(dec_us), "plan_us": med(plan_us),
+            "partition_us": med(part_us), "reduce_us": med(red_us),
+            "partition_us_mean": statistics.fmean(part_us),
+            "step_us_p10": float(np.percentile(step_us, 10)),
+            "step_us_p90": float(np.percentile(step_us, 90)),
+            "wall_us_per_step_incl_flush": wall / args.steps * 1e6,
+            "step_GBps": kvb / med(step_us) / 1e3,
+            "decode_GBps": kvb / med(dec_us) / 1e3,
+            "partition_GBps": kvb / statistics.fmean(part_us) / 1e3,
+        }
+        r["step_frac_of_peak"] = r["step_GBps"] / HBM_PEAK_GBS
+        r["decode_frac_of_peak"] = r["decode_GBps"] / HBM_PEAK_GBS
+        r["variant"] = int(plan.c.variant)
+        r["grid"] = int(plan.c.grid)
+        results[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+        log(f"{name}: step {r['step_us']:.1f}us (plan {r['plan_us']:.1f}, partition "
+            f"{r['partition_us']:.1f}, reduce {r['reduce_us']:.1f}) -> {r['step_GBps']:.0f} GB/s "
+            f"step, {r['decode_GBps']:.0f} GB/s decode")
+        if name == HEADLINE:
+            keep = dict(w=w, out=out.cpu(), spec=spec)
+        del d, ws, out, w
+        torch.cuda.empty_cache()
+
+    head = HEADLINE if HEADLINE in results else names[0]
+    hr = results[head]
+    spec = W.CONFIGS[head]
+    cpu = None
+    parity = None
+    if keep and not args.no_cpu_baseline:
+        cpu, parity = cpu_baseline(keep, args.cpu_seconds)
+    line = {
+        "metric": METRIC,
+        "value": round(hr["step_GBps"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(hr["step_us"] / 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{head}: batch {spec.batch}, q_len {spec.q_len}, {spec.num_q_heads} query "
+                        f"heads / {spec.num_kv_heads} kv heads, head_dim {spec.head_dim}, page "
+                        f"{spec.page_size}, context U[{spec.ctx_lo},{spec.ctx_hi}], partition "
+                        f"{args.partition or spec.partition_size}, seed {args.seed}",
+            "kv_bytes": hr["kv_bytes"],
+            "latency_us": hr["step_us"],
+            "decode_latency_us": hr["decode_us"],
+            "frac_of_hbm_peak": round(hr["step_frac_of_peak"], 4),
+            "timing": "median of HIP-event step times (plan + partition + reduce) on the launch "
+                      "stream; 1 GiB cache flush before each step, outside the events",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "partition",
+            "achieved": round(hr["partition_GBps"], 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(hr["partition_GBps"] / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "bytes_per_launch": hr["kv_bytes"],
+            "mean_launch_us": hr["partition_us_mean"],
+        },
+        "cpu_baseline": cpu,
+        "parity_sample": parity,
+        "per_config": results,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(keep, seconds):
+    """The CPU oracle, as it stands, on a bounded sample of the headline
+    workload's sequences; its outputs also check the GPU's on that sample."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import workloads as W
+
+    w, spec, gout = keep["w"], keep["spec"], keep["out"]
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    ctx = w.context_lens.tolist()
+    order = list(range(spec.batch))
+    done, t_total, kv_total, worst = [], 0.0, 0, 0.0
+    for b in order:
+        sub = W.Workload(W.scaled(spec, batch=1), w.seed, w.q[b:b + 1], w.k_cache, w.v_cache,
+                         w.block_table[b:b + 1], w.context_lens[b:b + 1], w.kv_scales, w.num_pages)
+        t0 = time.perf_counter()
+        want, _ = oracle.decode(sub.q, sub.k_cache, sub.v_cache, sub.block_table,
+                                sub.context_lens, spec.q_len, spec.scale, spec.page_size,
+                                spec.kv_dtype, spec.kv_scale_mode, sub.kv_scales)
+        t_total += time.perf_counter() - t0
+        kv_total += sub.kv_bytes()
+        got = gout[b:b + 1].float().numpy().astype(np.float64)
+        tol = 2e-2 if spec.kv_dtype == W.KV_FP8 else 8e-3
+        bad = np.abs(got - want) > tol + tol * np.abs(want)
+        worst = max(worst, float(np.abs(got - want).max()))
+        if bad.any() or not np.isfinite(got).all():
+            raise SystemExit(f"parity failure on sequence {b} of the benchmark workload")
+        done.append(b)
+        if t_total >= seconds:
+            break
+    log(f"cpu oracle: {len(done)} sequences, {kv_total / 1e6:.1f} MB KV in {t_total:.1f}s on "
+        f"{cores} threads")
+    cpu = {"value": round(kv_total / t_total / 1e9, 4), "unit": "GB/s", "cores": cores,
+           "kind": "oracle",
+           "sample": f"{len(done)} of {spec.batch} sequences of the headline workload "
+                     f"({sum(ctx[b] for b in done)} context tokens, {kv_total} KV bytes), "
+                     f"float64 NumPy oracle, {t_total:.1f}s"}
+    parity = {"sequences_checked": len(done), "max_abs_err": worst,
+              "tolerance": "atol = rtol = 8e-3 (bf16 KV)"}
+    return cpu, parity
+
+
+if __name__ == "__main__":
+    main()

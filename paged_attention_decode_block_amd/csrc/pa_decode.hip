@@ -52,6 +52,15 @@ __device__ __forceinline__ u32x4 ld16(const uint8_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
+// Load of wave-uniform, read-only metadata (segments, context lengths,
+// block-table entries, per-tensor scales) through the constant address space:
+// the compiler issues it as a scalar load, counted apart from the K/V vector
+// loads, so waiting for it never drains the K/V prefetch.
+template <typename T>
+__device__ __forceinline__ T ldu(const T* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) T*)(p))[i];
+}
+
 // 8 E4M3FN bytes -> 8 bf16 (exact: every finite E4M3FN value is a bf16 value).
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
   const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(lo), false);
@@ -88,14 +97,40 @@ __device__ __forceinline__ constexpr int qk_dim(int kc, int j) {
   return FP8 ? 64 * (kc >> 1) + 16 * j + 8 * (kc & 1) : 32 * kc + 8 * j;
 }
 
+// Buffer resources. A raw (unswizzled) buffer load returns zeros for bytes at
+// or past num_records without touching memory; the decode sizes each block's
+// resource to its live rows, so dead rows and dead blocks read as zeros and
+// every step issues the same number of loads.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int32_t kRsrcWord3 = 0x00020000;  // gfx9 family: 32-bit data format
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), kRsrcWord3);
+}
+
+// Values the compiler cannot prove wave-uniform (they pass a per-lane branch)
+// but are: pin them to scalar registers so buffer resources stay scalar.
+__device__ __forceinline__ int32_t uni(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ __forceinline__ uint64_t uni64(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+
 template <int D, bool FP8, int NB, int SM>
 struct Stage {
   static constexpr int LPB = D * (FP8 ? 1 : 2) / 64;
-  static constexpr int NS = SM == PA_SCALE_PER_TOKEN_HEAD ? NB : 0;
+  static constexpr int NS = SM == PA_SCALE_PER_TOKEN_HEAD ? NB : 1;
   u32x4 k[NB][LPB];
   u32x4 v[NB][LPB];
-  f32x4 ks[NS > 0 ? NS : 1];  // per-token K scales of the lane's S^T tokens
-  f32x4 vs[NS > 0 ? NS : 1];
+  f32x4 ks[NS];  // per-token K scales of the lane's S^T tokens
+  f32x4 vs[NS];
 };
 
 // One entry of a wave's chunk stream (wave-uniform values).
@@ -113,13 +148,14 @@ struct Cursor {
 };
 
 __device__ __forceinline__ void cursor_load(Cursor& c, const DecodeArgs& a, int wave) {
-  const Span sp = a.segs[c.s];
-  c.b = sp.pair / a.num_kv_heads;
-  c.g = sp.pair - c.b * a.num_kv_heads;
-  c.tb = sp.tok_begin;
-  c.te = sp.tok_end;
-  c.slot = sp.slot;
-  c.ctx = a.context_lens[c.b];
+  typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+  const i32x4 sp = ldu(reinterpret_cast<const i32x4*>(a.segs), c.s);  // pair, begin, end, slot
+  c.b = sp.x / a.num_kv_heads;
+  c.g = sp.x - c.b * a.num_kv_heads;
+  c.tb = sp.y;
+  c.te = sp.z;
+  c.slot = sp.w;
+  c.ctx = ldu(a.context_lens, c.b);
   c.k = wave;
 }
 
@@ -151,71 +187,78 @@ __device__ __forceinline__ Entry cursor_take(Cursor& c, const DecodeArgs& a, int
   return e;
 }
 
+// Block-table entries of an entry's 16-token blocks (one per block: a block
+// never crosses a page). Vector loads of a uniform address, issued a step
+// before the K/V loads that use them; entries past the row read as 0.
 template <int NB>
-__device__ __forceinline__ void load_pages(const DecodeArgs& a, const Entry& e, int32_t (&pg)[NB]) {
+__device__ __forceinline__ void load_pages(const DecodeArgs& a, const Entry& e, uint32_t (&pg)[NB]) {
+  const bool live = e.live && e.data;
+  const rsrc_t r = make_rsrc(a.block_table + static_cast<int64_t>(e.b) * a.max_pages,
+                             live ? static_cast<uint32_t>(a.max_pages) * 4u : 0u);
 #pragma unroll
   for (int blk = 0; blk < NB; ++blk) {
-    const int32_t t = e.tc0 + 16 * blk;
-    pg[blk] = (e.live && e.data && t < e.te)
-                  ? a.block_table[static_cast<int64_t>(e.b) * a.max_pages + (t >> a.ps_log2)]
-                  : 0;
+    const uint32_t idx = static_cast<uint32_t>(max(e.tc0 + 16 * blk, 0)) >> a.ps_log2;
+    pg[blk] = __builtin_amdgcn_raw_buffer_load_b32(r, idx * 4u, 0, 0);
   }
 }
 
 template <int D, bool FP8, int NB, int SM>
-__device__ __forceinline__ void issue_kv(const DecodeArgs& a, const Entry& e, const int32_t (&pg)[NB],
+__device__ __forceinline__ void issue_kv(const DecodeArgs& a, const Entry& e, const uint32_t (&pgv)[NB],
                                          Stage<D, FP8, NB, SM>& st, int lane) {
   constexpr int ROWB = D * (FP8 ? 1 : 2);
   constexpr int LPB = ROWB / 64;
   const int c = lane & 15, j = lane >> 4;
   const int ps_mask = (1 << a.ps_log2) - 1;
+  // Lane (c, j) reads bytes [64 i + 16 j, +16) of row c of each 16-token
+  // block; the block's resource covers only its rows before the segment end.
+  const uint32_t lane_off = static_cast<uint32_t>(c * ROWB + 16 * j);
 #pragma unroll
   for (int blk = 0; blk < NB; ++blk) {
     const int32_t t0 = e.tc0 + 16 * blk;
-    int32_t page = pg[blk];
-    bool page_ok = true;
-    if (a.debug_bounds && t0 < e.te && (page < 0 || page >= a.num_pages)) {
-      page_ok = false;
-      if (lane == 0) atomicOr(a.status + ST_BITS, PA_DEV_BAD_PAGE);
+    int32_t nlive = (e.live && e.data) ? min(max(e.te - t0, 0), 16) : 0;
+    int32_t page = static_cast<int32_t>(__builtin_amdgcn_readfirstlane(pgv[blk]));
+    if (a.debug_bounds && nlive > 0 && (page < 0 || page >= a.num_pages)) {
+      nlive = 0;
+      atomicOr(a.status + ST_BITS, PA_DEV_BAD_PAGE);
     }
-    const uint64_t row0 = cache_row(page, e.g, t0 & ps_mask, a.num_kv_heads, a.ps_log2);
-    const bool ok = page_ok && (t0 + c < e.te);
-    const uint64_t off = (row0 + c) * ROWB + 16 * j;
-    const uint8_t* kp = a.k_cache + off;
-    const uint8_t* vp = a.v_cache + off;
+    nlive = uni(nlive);
+    if (nlive == 0) page = 0;
+    const uint64_t row0 = uni64(cache_row(page, e.g, t0 & ps_mask, a.num_kv_heads, a.ps_log2));
+    const rsrc_t rk = make_rsrc(a.k_cache + row0 * ROWB, static_cast<uint32_t>(nlive * ROWB));
+    const rsrc_t rv = make_rsrc(a.v_cache + row0 * ROWB, static_cast<uint32_t>(nlive * ROWB));
 #pragma unroll
     for (int i = 0; i < LPB; ++i) {
-      st.k[blk][i] = ok ? ld16(kp + 64 * i) : u32x4{0, 0, 0, 0};
-      st.v[blk][i] = ok ? ld16(vp + 64 * i) : u32x4{0, 0, 0, 0};
+      st.k[blk][i] = bload16(rk, lane_off + 64 * i);
+      st.v[blk][i] = bload16(rv, lane_off + 64 * i);
     }
     if constexpr (SM == PA_SCALE_PER_TOKEN_HEAD) {
-      const bool ok4 = page_ok && (t0 + 4 * j < e.te);
-      const uint64_t srow = row0 + 4 * j;
-      const uint64_t vbase = static_cast<uint64_t>(a.num_pages) * a.num_kv_heads << a.ps_log2;
-      st.ks[blk] = ok4 ? *reinterpret_cast<const f32x4*>(a.kv_scales + srow) : f32x4{0, 0, 0, 0};
-      st.vs[blk] = ok4 ? *reinterpret_cast<const f32x4*>(a.kv_scales + vbase + srow)
-                       : f32x4{0, 0, 0, 0};
+      const uint64_t vplane = static_cast<uint64_t>(a.num_pages) * a.num_kv_heads << a.ps_log2;
+      const rsrc_t rks = make_rsrc(a.kv_scales + row0, static_cast<uint32_t>(nlive * 4));
+      const rsrc_t rvs = make_rsrc(a.kv_scales + vplane + row0, static_cast<uint32_t>(nlive * 4));
+      st.ks[blk] = __builtin_bit_cast(f32x4, bload16(rks, 16u * j));
+      st.vs[blk] = __builtin_bit_cast(f32x4, bload16(rvs, 16u * j));
     }
   }
 }
 
 template <int D, bool FP8, int RT>
 __device__ __forceinline__ void load_q(const DecodeArgs& a, const Entry& e, int lane,
-                                       bf16x8 (&qn)[RT * (D / 32)]) {
+                                       bf16x8 (&qr)[RT * (D / 32)]) {
   constexpr int KC = D / 32;
   const int c = lane & 15, j = lane >> 4;
+  const int64_t seq_elems = static_cast<int64_t>(a.q_len) * a.num_q_heads * D;
+  const rsrc_t rq = make_rsrc(a.q + e.b * seq_elems, static_cast<uint32_t>(seq_elems * 2));
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    const int r = 16 * rt + c;
-    const bool ok = r < a.rows;
-    const int i = ok ? r / a.group : 0;
-    const int h = e.g * a.group + (ok ? r - i * a.group : 0);
-    const uint16_t* qp = a.q + ((static_cast<int64_t>(e.b) * a.q_len + i) * a.num_q_heads + h) * D;
+    // rows past R (MFMA padding) reuse the last real row: finite values whose
+    // results are never written
+    const int r = min(16 * rt + c, a.rows - 1);
+    const int i = r / a.group;
+    const int h = e.g * a.group + (r - i * a.group);
+    const uint32_t off = static_cast<uint32_t>((i * a.num_q_heads + h) * D) * 2u;
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      u32x4 w = ok ? *reinterpret_cast<const u32x4*>(qp + qk_dim<FP8>(kc, j)) : u32x4{0, 0, 0, 0};
-      qn[rt * KC + kc] = __builtin_bit_cast(bf16x8, w);
-    }
+    for (int kc = 0; kc < KC; ++kc)
+      qr[rt * KC + kc] = __builtin_bit_cast(bf16x8, bload16(rq, off + 2u * qk_dim<FP8>(kc, j)));
   }
 }
 
@@ -223,6 +266,8 @@ template <int D, bool FP8, int SM, int RT, int NB, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void partition_kernel(DecodeArgs a) {
   using C = Cfg<D, FP8, RT, NB, NW>;
   constexpr int KC = C::KC, DT = C::DT, TC = C::TC, LPB = C::LPB;
+  // Prefetch the next segment's Q into registers when they are affordable.
+  constexpr bool QPF = RT <= 2;
 
   __shared__ __attribute__((aligned(16))) uint8_t lds_waves[NW * C::WBYTES];
   __shared__ float st_m[NW][RT * 16];
@@ -234,8 +279,8 @@ __global__ __launch_bounds__(NW * 64, 1) void partition_kernel(DecodeArgs a) {
   const int w = blockIdx.x;
 
   Cursor cur;
-  cur.s = a.wg_seg_begin[w];
-  cur.s_end = a.wg_seg_begin[w + 1];
+  cur.s = ldu(a.wg_seg_begin, w);
+  cur.s_end = ldu(a.wg_seg_begin, w + 1);
   if (cur.s >= cur.s_end) return;
   cur.live = 1;
   cursor_load(cur, a, wave);
@@ -245,8 +290,8 @@ __global__ __launch_bounds__(NW * 64, 1) void partition_kernel(DecodeArgs a) {
   float qk_f = a.qk_scale_log2;
   float out_f = a.out_scale;
   if constexpr (SM == PA_SCALE_PER_TENSOR) {
-    qk_f *= a.kv_scales[0];
-    out_f = a.kv_scales[1];
+    qk_f *= ldu(a.kv_scales, 0);
+    out_f = ldu(a.kv_scales, 1);
   }
 
   // Query index of each of this lane's rows (rows past R see every key).
@@ -264,22 +309,33 @@ __global__ __launch_bounds__(NW * 64, 1) void partition_kernel(DecodeArgs a) {
   Entry e2 = cursor_take<TC, NW>(cur, a, wave);
 
   bf16x8 q[RT * KC];
-  Stage<D, FP8, NB, SM> sA, sB;
-  int32_t pg[NB];
+  bf16x8 qn[QPF ? RT * KC : 1];
+  Stage<D, FP8, NB, SM> sA = {}, sB = {};
+  uint32_t pgX[NB], pgY[NB];
 
-  // prologue: K/V of entry 0, pages of entry 1
-  load_pages<NB>(a, e0, pg);
-  if (e0.data) issue_kv<D, FP8, NB, SM>(a, e0, pg, sA, lane);
-  load_pages<NB>(a, e1, pg);
+  // prologue, in the steady state's issue order (so that every later wait
+  // has the same number of younger loads on every path): pages of entry 0,
+  // Q of entry 0, pages of entry 1, K/V of entry 0
+  load_pages<NB>(a, e0, pgY);
+  if constexpr (QPF) load_q<D, FP8, RT>(a, e0, lane, qn);
+  load_pages<NB>(a, e1, pgX);
+  issue_kv<D, FP8, NB, SM>(a, e0, pgY, sA, lane);
 
   float m[RT], l[RT];
   f32x4 o[DT][RT];
 
-  auto step = [&](Stage<D, FP8, NB, SM>& cs, Stage<D, FP8, NB, SM>& ns) {
+  // One step of a wave's pipeline. Issue order: pages of e2, Q of e1 (if it
+  // opens a segment), K/V of e1; then the math on e0, whose K/V were issued a
+  // step earlier. Every wait is on loads issued at least one step before.
+  auto step = [&](Stage<D, FP8, NB, SM>& cs, Stage<D, FP8, NB, SM>& ns, uint32_t (&pgc)[NB],
+                  uint32_t (&pgn)[NB]) {
     if (e0.first) {
-      // Q rows of the new segment's pair (issued before the next chunk's
-      // K/V so waiting for them does not wait for that prefetch)
-      load_q<D, FP8, RT>(a, e0, lane, q);
+      if constexpr (QPF) {
+#pragma unroll
+        for (int x = 0; x < RT * KC; ++x) q[x] = qn[x];
+      } else {
+        load_q<D, FP8, RT>(a, e0, lane, q);
+      }
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         m[rt] = neg_inf();
@@ -288,9 +344,11 @@ __global__ __launch_bounds__(NW * 64, 1) void partition_kernel(DecodeArgs a) {
         for (int dt = 0; dt < DT; ++dt) o[dt][rt] = f32x4{0, 0, 0, 0};
       }
     }
-    // stage 1: K/V of the next chunk; stage 0: block-table pages two chunks ahead
-    if (e1.live && e1.data) issue_kv<D, FP8, NB, SM>(a, e1, pg, ns, lane);
-    load_pages<NB>(a, e2, pg);
+    load_pages<NB>(a, e2, pgn);
+    if constexpr (QPF) {
+      if (e1.live && e1.first) load_q<D, FP8, RT>(a, e1, lane, qn);
+    }
+    issue_kv<D, FP8, NB, SM>(a, e1, pgc, ns, lane);
 
     if (e0.data) {
       // ---- S^T = K Q^T: lane holds tokens 16 blk + 4 j + i of row 16 rt + c
@@ -314,7 +372,8 @@ __global__ __launch_bounds__(NW * 64, 1) void partition_kernel(DecodeArgs a) {
         }
       }
 
-      // ---- scale, causal mask, online softmax (exp2 domain)
+      // ---- scale, causal mask, online softmax (exp2 domain). Keys past the
+      // segment end were read as zeros; the mask drops them.
       const bool full = (e0.tc0 + TC <= e0.te) && (e0.tc0 + TC - 1 <= e0.ctx - a.q_len);
       constexpr bool per_tok = SM == PA_SCALE_PER_TOKEN_HEAD;
       float pv[NB][RT][4];
@@ -346,12 +405,8 @@ __global__ __launch_bounds__(NW * 64, 1) void partition_kernel(DecodeArgs a) {
           for (int i = 0; i < 4; ++i) {
             const float p = __builtin_amdgcn_exp2f(x[blk][i] - mu);
             ps += p;
-            float q2 = p;
-            if constexpr (per_tok) {
-              q2 = p * cs.vs[blk][i];
-              if (!full) q2 = (e0.tc0 + 16 * blk + 4 * j + i <= lim) ? q2 : 0.f;
-            }
-            pv[blk][rt][i] = q2;
+            if constexpr (per_tok) pv[blk][rt][i] = p * cs.vs[blk][i];
+            else pv[blk][rt][i] = p;
           }
         }
         l[rt] = l[rt] * alpha + ps;
@@ -437,13 +492,11 @@ __global__ __launch_bounds__(NW * 64, 1) void partition_kernel(DecodeArgs a) {
 
     if (e0.last) {
       // ---- merge the NW waves' (max, sum, O) of this segment
-      float lt[RT];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         float v = l[rt];
         v += __shfl_xor(v, 16);
         v += __shfl_xor(v, 32);
-        lt[rt] = v;
         if (j == 0) {
           st_m[wave][16 * rt + c] = m[rt];
           st_l[wave][16 * rt + c] = v;
@@ -512,41 +565,74 @@ __global__ __launch_bounds__(NW * 64, 1) void partition_kernel(DecodeArgs a) {
   };
 
   for (;;) {
-    step(sA, sB);
+    step(sA, sB, pgX, pgY);
     if (!e0.live) break;
-    step(sB, sA);
+    step(sB, sA, pgY, pgX);
     if (!e0.live) break;
   }
 }
 
-// One workgroup per (sequence, kv head) pair; pairs with a single segment
-// were finished by the partition pass.
+// Log-sum-exp reduce: one workgroup per (pair, block of 16 query rows);
+// pairs with a single segment were finished by the partition pass. For row r
+// of a split pair with partials (O_s, lse_s): M = max lse_s,
+// w_s = exp(lse_s - M), out = sum w_s O_s / sum w_s ("[Kernel][Perf] Optimize
+// paged-attention metadata decode", ROCm/FlyDSL PR #910, overview: the split
+// reduction kernel). Thread (row, 8 dims) walks the slots four at a time so
+// several partial loads are in flight.
 constexpr int kReduceThreads = 256;
+constexpr int kReduceRows = 16;
 
 template <int D>
 __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(DecodeArgs a) {
   const int p = blockIdx.x;
-  const int n = a.nseg[p];
+  const int n = ldu(a.nseg, p);
   if (n <= 1) return;
-  const int base = a.seg_base[p];
+  const int base = ldu(a.seg_base, p);
   const int b = p / a.num_kv_heads;
   const int g = p - b * a.num_kv_heads;
   const int R = a.rows;
-  for (int u = threadIdx.x; u < R * (D / 8); u += kReduceThreads) {
-    const int r = u / (D / 8);
-    const int d0 = (u - r * (D / 8)) * 8;
+  constexpr int U = D / 8;  // 8-dim units per row
+  for (int u = threadIdx.x; u < kReduceRows * U; u += kReduceThreads) {
+    const int r = blockIdx.y * kReduceRows + u / U;
+    const int d0 = (u % U) * 8;
+    if (r >= R) continue;
+    const float* lse = a.partial_lse + static_cast<int64_t>(base) * R + r;
     float M = neg_inf();
-    for (int s = 0; s < n; ++s) M = fmaxf(M, a.partial_lse[static_cast<int64_t>(base + s) * R + r]);
+    int s = 0;
+    for (; s + 4 <= n; s += 4) {
+      const float l0 = lse[(s + 0) * R], l1 = lse[(s + 1) * R];
+      const float l2 = lse[(s + 2) * R], l3 = lse[(s + 3) * R];
+      M = fmaxf(M, fmaxf(fmaxf(l0, l1), fmaxf(l2, l3)));
+    }
+    for (; s < n; ++s) M = fmaxf(M, lse[s * R]);
     const float Mu = M == neg_inf() ? 0.f : M;
+    const float* po = a.partial_o + (static_cast<int64_t>(base) * R + r) * D + d0;
+    const int64_t so = static_cast<int64_t>(R) * D;  // slot stride in floats
     float W = 0.f;
     f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
-    for (int s = 0; s < n; ++s) {
-      const int64_t row = static_cast<int64_t>(base + s) * R + r;
-      const float wgt = __builtin_amdgcn_exp2f((a.partial_lse[row] - Mu) * kLog2e);
+    s = 0;
+    for (; s + 4 <= n; s += 4) {
+      f32x4 x[4][2];
+      float wt[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        wt[t] = lse[(s + t) * R];
+        x[t][0] = *reinterpret_cast<const f32x4*>(po + (s + t) * so);
+        x[t][1] = *reinterpret_cast<const f32x4*>(po + (s + t) * so + 4);
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float wgt = __builtin_amdgcn_exp2f((wt[t] - Mu) * kLog2e);
+        W += wgt;
+        acc0 += wgt * x[t][0];
+        acc1 += wgt * x[t][1];
+      }
+    }
+    for (; s < n; ++s) {
+      const float wgt = __builtin_amdgcn_exp2f((lse[s * R] - Mu) * kLog2e);
       W += wgt;
-      const float* src = a.partial_o + row * D + d0;
-      acc0 += wgt * *reinterpret_cast<const f32x4*>(src);
-      acc1 += wgt * *reinterpret_cast<const f32x4*>(src + 4);
+      acc0 += wgt * *reinterpret_cast<const f32x4*>(po + s * so);
+      acc1 += wgt * *reinterpret_cast<const f32x4*>(po + s * so + 4);
     }
     const float inv = W > 0.f ? 1.f / W : 0.f;
     acc0 *= inv;
@@ -629,10 +715,11 @@ hipError_t launch_partition(int vi, const DecodeArgs& a, int grid, hipStream_t s
 }
 
 hipError_t launch_reduce(const DecodeArgs& a, int head_dim, int num_pairs, hipStream_t s) {
+  const dim3 grid(num_pairs, (a.rows + kReduceRows - 1) / kReduceRows);
   if (head_dim == 128)
-    hipLaunchKernelGGL(reduce_kernel<128>, dim3(num_pairs), dim3(kReduceThreads), 0, s, a);
+    hipLaunchKernelGGL(reduce_kernel<128>, grid, dim3(kReduceThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(reduce_kernel<256>, dim3(num_pairs), dim3(kReduceThreads), 0, s, a);
+    hipLaunchKernelGGL(reduce_kernel<256>, grid, dim3(kReduceThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -8,8 +8,9 @@
 // ranges per workgroup, segments = same-pair runs inside a range, partial
 // slots only for pairs split over several workgroups.
 //
-// Method: two prefix sums (items per sequence, segments per pair) and a closed
-// form per item. With N items over G workgroups, workgroup w starts at
+// Method: prefix sums (items per sequence, segments per pair, both owned by
+// thread chunks) and a closed form per item; each thread writes a contiguous
+// run of items. With N items over G workgroups, workgroup w starts at
 // lo(w) = floor(w N / G) and item x belongs to owner(x) = floor(((x+1) G - 1) / N),
 // the largest w with lo(w) <= x. When N >= G every range is non-empty, so
 // the segment index of item x inside its pair (first item A) is
@@ -21,33 +22,32 @@ namespace pa {
 namespace {
 
 constexpr int kPlanThreads = 1024;
+constexpr int kPlanWaves = kPlanThreads / 64;
+constexpr int kLdsSeqs = 4096;   // sequences whose item bases are kept in LDS
+constexpr int kLdsPairs = 4096;  // pairs whose segment counts / bases are kept in LDS
 
-// In-place exclusive prefix sum of data[0, n) in global memory; returns the
-// total. Thread t owns a contiguous chunk; chunk sums are scanned in LDS.
-__device__ int32_t block_exclusive_scan(int32_t* data, int32_t n, int32_t* lds) {
-  const int tid = threadIdx.x;
-  const int per = (n + kPlanThreads - 1) / kPlanThreads;
-  const int lo = min(n, tid * per);
-  const int hi = min(n, lo + per);
-  int32_t sum = 0;
-  for (int x = lo; x < hi; ++x) sum += data[x];
-  lds[tid] = sum;
-  __syncthreads();
-  for (int off = 1; off < kPlanThreads; off <<= 1) {
-    const int32_t v = tid >= off ? lds[tid - off] : 0;
-    __syncthreads();
-    lds[tid] += v;
-    __syncthreads();
+// Exclusive prefix sum of one value per thread over the workgroup: a wave
+// scan with lane shuffles, then the 16 wave totals through LDS.
+__device__ int32_t block_exclusive_scan(int32_t v, int32_t* wsum, int32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int32_t x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t y = __shfl_up(x, off);
+    if (lane >= off) x += y;
   }
-  int32_t run = lds[tid] - sum;
-  const int32_t total = lds[kPlanThreads - 1];
-  for (int x = lo; x < hi; ++x) {
-    const int32_t v = data[x];
-    data[x] = run;
-    run += v;
-  }
+  if (lane == 63) wsum[wave] = x;
   __syncthreads();
-  return total;
+  int32_t before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kPlanWaves; ++w) {
+    const int32_t s = wsum[w];
+    tot += s;
+    before += w < wave ? s : 0;
+  }
+  *total = tot;
+  __syncthreads();
+  return before + x - v;
 }
 
 __device__ __forceinline__ int32_t wg_lo(int64_t w, int64_t N, int64_t G) {
@@ -62,51 +62,36 @@ __device__ __forceinline__ int32_t seg_index(int32_t x, int32_t A, int64_t N, in
   return N >= G ? owner(x, N, G) - owner(A, N, G) : x - A;
 }
 
-// Largest b in [0, B) with batch_base[b] <= x (batch_base has B + 1 entries).
-__device__ __forceinline__ int32_t find_seq(const int32_t* batch_base, int32_t B, int32_t x) {
-  int lo = 0, hi = B;  // invariant: batch_base[lo] <= x < batch_base[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (batch_base[mid] <= x) lo = mid; else hi = mid;
-  }
-  return lo;
-}
-
-struct ItemPos {
-  int32_t pair, A, n, k, ctx;
-};
-
-__device__ __forceinline__ ItemPos locate(const PlanArgs& a, int32_t x) {
-  const int32_t b = find_seq(a.batch_base, a.batch, x);
-  const int32_t base = a.batch_base[b];
-  const int32_t n = (a.batch_base[b + 1] - base) / a.num_kv_heads;
-  const int32_t r = x - base;
-  const int32_t g = r / n;
-  ItemPos ip;
-  ip.pair = b * a.num_kv_heads + g;
-  ip.A = base + g * n;
-  ip.n = n;
-  ip.k = r - g * n;
-  ip.ctx = a.context_lens[b];
-  return ip;
-}
+__device__ __forceinline__ int32_t items_of(int32_t ctx, int32_t P) { return (max(ctx, 0) + P - 1) / P; }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
-  __shared__ int32_t lds[kPlanThreads];
+  __shared__ int32_t wsum[kPlanWaves];
   __shared__ int32_t bad;
+  __shared__ int32_t l_base[kLdsSeqs + 1];
+  __shared__ int32_t l_nseg[kLdsPairs], l_sbase[kLdsPairs], l_pbase[kLdsPairs];
   const int tid = threadIdx.x;
   const int32_t B = a.batch, H = a.num_kv_heads, P = a.partition, G = a.grid;
   const int32_t pairs = B * H;
+  // per-sequence / per-pair tables: LDS when they fit, else the workspace
+  int32_t* base_t = B < kLdsSeqs ? l_base : a.batch_base;
+  int32_t* nseg_t = pairs <= kLdsPairs ? l_nseg : a.nseg;
+  int32_t* sbase_t = pairs <= kLdsPairs ? l_sbase : a.seg_base;
+  int32_t* pbase_t = pairs <= kLdsPairs ? l_pbase : a.pseg_base;
   if (tid == 0) bad = 0;
   __syncthreads();
 
-  // 1. validate context lengths; items per sequence = H * ceil(ctx / P)
-  for (int b = tid; b < B; b += kPlanThreads) {
+  // 1. thread t owns sequences [b_lo, b_hi): validate, count items, and
+  //    find the first item of each by a prefix sum
+  const int32_t per_b = (B + kPlanThreads - 1) / kPlanThreads;
+  const int32_t b_lo = min(B, tid * per_b), b_hi = min(B, b_lo + per_b);
+  int32_t sum = 0;
+  for (int32_t b = b_lo; b < b_hi; ++b) {
     const int32_t c = a.context_lens[b];
     if (c < max(1, a.q_len) || c > a.capacity) atomicOr(&bad, 1);
-    a.batch_base[b] = H * ((max(c, 0) + P - 1) / P);
+    sum += H * items_of(c, P);
   }
-  __syncthreads();
+  int32_t N = 0;
+  const int32_t first = block_exclusive_scan(sum, wsum, &N);
   if (bad) {
     for (int i = tid; i <= G; i += kPlanThreads) { a.wg_begin[i] = 0; a.wg_seg_begin[i] = 0; }
     for (int i = tid; i < pairs; i += kPlanThreads) a.nseg[i] = 0;
@@ -119,61 +104,115 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     }
     return;
   }
-  const int32_t N = block_exclusive_scan(a.batch_base, B, lds);
-  if (tid == 0) a.batch_base[B] = N;
-  __syncthreads();
 
-  // 2. segments per pair, then slot bases (split pairs) and segment bases (all)
-  for (int p = tid; p < pairs; p += kPlanThreads) {
-    const int32_t b = p / H, g = p - b * H;
-    const int32_t n = (a.batch_base[b + 1] - a.batch_base[b]) / H;
-    const int32_t A = a.batch_base[b] + g * n;
-    const int32_t ns = seg_index(A + n - 1, A, N, G) + 1;
-    a.nseg[p] = ns;
-    a.seg_base[p] = ns > 1 ? ns : 0;
-    a.pseg_base[p] = ns;
+  // 2. the same thread's pairs: segment counts, then slot bases (split pairs
+  //    only) and segment bases by two more prefix sums
+  int32_t split = 0, all = 0;
+  {
+    int32_t A = first;
+    for (int32_t b = b_lo; b < b_hi; ++b) {
+      const int32_t n = items_of(a.context_lens[b], P);
+      for (int32_t g = 0; g < H; ++g, A += n) {
+        const int32_t ns = seg_index(A + n - 1, A, N, G) + 1;
+        split += ns > 1 ? ns : 0;
+        all += ns;
+      }
+    }
   }
-  __syncthreads();
-  const int32_t slots = block_exclusive_scan(a.seg_base, pairs, lds);
-  const int32_t S = block_exclusive_scan(a.pseg_base, pairs, lds);
+  int32_t slots = 0, S = 0;
+  int32_t run_split = block_exclusive_scan(split, wsum, &slots);
+  int32_t run_all = block_exclusive_scan(all, wsum, &S);
+  {
+    int32_t A = first;
+    for (int32_t b = b_lo; b < b_hi; ++b) {
+      const int32_t n = items_of(a.context_lens[b], P);
+      base_t[b] = A;
+      a.batch_base[b] = A;
+      for (int32_t g = 0; g < H; ++g, A += n) {
+        const int32_t p = b * H + g;
+        const int32_t ns = seg_index(A + n - 1, A, N, G) + 1;
+        nseg_t[p] = ns;
+        sbase_t[p] = run_split;
+        pbase_t[p] = run_all;
+        a.nseg[p] = ns;
+        a.seg_base[p] = run_split;
+        a.pseg_base[p] = run_all;
+        run_split += ns > 1 ? ns : 0;
+        run_all += ns;
+      }
+    }
+  }
   if (tid == 0) {
+    base_t[B] = N;
+    a.batch_base[B] = N;
     a.seg_base[pairs] = slots;
     a.pseg_base[pairs] = S;
   }
   __syncthreads();
 
-  // 3. items, and the segment each segment-starting item opens
-  for (int32_t x = tid; x < N; x += kPlanThreads) {
-    const ItemPos ip = locate(a, x);
-    const int32_t j = seg_index(x, ip.A, N, G);
-    const int32_t ns = a.nseg[ip.pair];
-    Span it;
-    it.pair = ip.pair;
-    it.tok_begin = ip.k * P;
-    it.tok_end = min((ip.k + 1) * P, ip.ctx);
-    it.slot = ns > 1 ? a.seg_base[ip.pair] + j : -1;
-    a.items[x] = it;
-    const int32_t w = owner(x, N, G);
-    if (x == ip.A || x == wg_lo(w, N, G)) {
-      const int32_t last = min(ip.A + ip.n, wg_lo(w + 1, N, G)) - 1;
-      Span sg = it;
-      sg.tok_end = min((last - ip.A + 1) * P, ip.ctx);
-      a.segs[a.pseg_base[ip.pair] + j] = sg;
+  // 3. thread t writes items [x0, x1): each item, the segment it opens, and
+  //    the segment-range start of every workgroup whose range starts there
+  const int32_t per_x = (N + kPlanThreads - 1) / kPlanThreads;
+  const int32_t x0 = min(N, tid * per_x), x1 = min(N, x0 + per_x);
+  if (x0 < x1) {
+    int lo = 0, hi = B;  // largest b with base_t[b] <= x0
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (base_t[mid] <= x0) lo = mid; else hi = mid;
+    }
+    int32_t b = lo;
+    int32_t ctx = a.context_lens[b];
+    int32_t n = items_of(ctx, P);
+    int32_t g = (x0 - base_t[b]) / n;
+    int32_t k = x0 - base_t[b] - g * n;
+    int32_t p = b * H + g;
+    int32_t A = base_t[b] + g * n;
+    int32_t ns = nseg_t[p], sb = sbase_t[p], pb = pbase_t[p];
+    for (int32_t x = x0; x < x1; ++x) {
+      const int32_t j = seg_index(x, A, N, G);
+      Span it;
+      it.pair = p;
+      it.tok_begin = k * P;
+      it.tok_end = min((k + 1) * P, ctx);
+      it.slot = ns > 1 ? sb + j : -1;
+      a.items[x] = it;
+      const int32_t w = owner(x, N, G);
+      const int32_t lo_w = wg_lo(w, N, G);
+      if (x == A || x == lo_w) {
+        const int32_t last = min(A + n, wg_lo(w + 1, N, G)) - 1;
+        Span sg = it;
+        sg.tok_end = min((last - A + 1) * P, ctx);
+        a.segs[pb + j] = sg;
+      }
+      if (x == lo_w) {
+        // workgroups ceil(x G / N) .. w all start their (possibly empty) range at x
+        const int32_t w0 = static_cast<int32_t>((static_cast<int64_t>(x) * G + N - 1) / N);
+        for (int32_t w2 = w0; w2 <= w; ++w2) a.wg_seg_begin[w2] = pb + j;
+      }
+      if (++k == n) {  // next pair: next kv head, or the next sequence
+        k = 0;
+        A += n;
+        if (++g == H) {
+          g = 0;
+          if (++b < B) {
+            ctx = a.context_lens[b];
+            n = items_of(ctx, P);
+          }
+        }
+        p = b * H + g;
+        if (x + 1 < x1) {
+          ns = nseg_t[p];
+          sb = sbase_t[p];
+          pb = pbase_t[p];
+        }
+      }
     }
   }
 
-  // 4. per-workgroup item and segment ranges
-  for (int32_t w = tid; w <= G; w += kPlanThreads) {
-    const int32_t lo = wg_lo(w, N, G);
-    a.wg_begin[w] = lo;
-    int32_t sb = S;
-    if (lo < N) {
-      const ItemPos ip = locate(a, lo);
-      sb = a.pseg_base[ip.pair] + seg_index(lo, ip.A, N, G);
-    }
-    a.wg_seg_begin[w] = sb;
-  }
+  // 4. item ranges
+  for (int32_t w = tid; w <= G; w += kPlanThreads) a.wg_begin[w] = wg_lo(w, N, G);
   if (tid == 0) {
+    a.wg_seg_begin[G] = S;
     a.status[ST_BITS] = 0;
     a.status[ST_ITEMS] = N;
     a.status[ST_SEGS] = S;

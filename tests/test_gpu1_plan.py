@@ -57,6 +57,14 @@ def test_plan_configs(name):
                    s.max_pages_per_seq, name=f"{name}/{seed}")
 
 
+def test_plan_tables_past_lds():
+    # more sequences / pairs than the plan kernel keeps in LDS: tables live in
+    # the workspace instead
+    r = random.Random(7)
+    _plan_case([r.randint(1, 64) for _ in range(5000)], 1, 16, 1, 16, 4, name="5000 sequences")
+    _plan_case([r.randint(1, 300) for _ in range(600)], 8, 32, 1, 16, 20, name="4800 pairs")
+
+
 def test_plan_edges():
     _plan_case([1], 1, 256, 1, 16, 1, name="one token")
     _plan_case([16] * 300, 1, 16, 1, 16, 1, name="one item per pair, N > G")
