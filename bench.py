@@ -48,6 +48,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle sample")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="run one 512 MiB device copy first (a known-size kernel for scaling "
+                        "rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     return p.parse_args()
 
 
@@ -74,6 +77,14 @@ def main():
         names.insert(0, HEADLINE)
     flush = None if args.no_flush else torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
     cus = pa.pa_query_device(0)
+    if args.calibrate_copy:
+        src = torch.ones(1 << 27, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration copy: 536870912 bytes read, 536870912 bytes written")
+        del src, dst
     results = {}
     keep = {}
     for name in names:

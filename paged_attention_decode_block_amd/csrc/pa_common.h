@@ -67,8 +67,9 @@ __device__ __forceinline__ uint64_t cache_row(int32_t page, int32_t kv_head, int
           << ps_log2) + static_cast<uint64_t>(slot);
 }
 
-// Decode kernel instantiations: head dim, KV element type, 16-row tiles of
-// query rows, 16-token blocks per chunk, waves per workgroup.
+// Decode kernel instantiations: head dim, KV element type, scale mode,
+// 16-row tiles of query rows, 16-token blocks per chunk, waves per
+// workgroup, K/V register stages of the load pipeline.
 struct Variant {
   int head_dim;
   int fp8;
@@ -76,6 +77,7 @@ struct Variant {
   int row_tiles;
   int blocks;
   int waves;
+  int stages;
 };
 
 int num_variants();

@@ -30,6 +30,8 @@
 //   * at a segment's end the NW waves merge their (max, sum, O) through LDS;
 //     an unsplit pair writes bf16 output, a split pair writes its partial O
 //     and log-sum-exp to its slot
+#include <type_traits>
+
 #include "pa_common.h"
 
 namespace pa {
@@ -212,30 +214,47 @@ __device__ __forceinline__ void issue_kv(const DecodeArgs& a, const Entry& e, co
   // Lane (c, j) reads bytes [64 i + 16 j, +16) of row c of each 16-token
   // block; the block's resource covers only its rows before the segment end.
   const uint32_t lane_off = static_cast<uint32_t>(c * ROWB + 16 * j);
+  rsrc_t rk[NB], rv[NB];
+  uint64_t row0[NB];
+  int32_t nlive[NB];
 #pragma unroll
   for (int blk = 0; blk < NB; ++blk) {
     const int32_t t0 = e.tc0 + 16 * blk;
-    int32_t nlive = (e.live && e.data) ? min(max(e.te - t0, 0), 16) : 0;
+    int32_t nl = (e.live && e.data) ? min(max(e.te - t0, 0), 16) : 0;
     int32_t page = static_cast<int32_t>(__builtin_amdgcn_readfirstlane(pgv[blk]));
-    if (a.debug_bounds && nlive > 0 && (page < 0 || page >= a.num_pages)) {
-      nlive = 0;
+    if (a.debug_bounds && nl > 0 && (page < 0 || page >= a.num_pages)) {
+      nl = 0;
       atomicOr(a.status + ST_BITS, PA_DEV_BAD_PAGE);
     }
-    nlive = uni(nlive);
-    if (nlive == 0) page = 0;
-    const uint64_t row0 = uni64(cache_row(page, e.g, t0 & ps_mask, a.num_kv_heads, a.ps_log2));
-    const rsrc_t rk = make_rsrc(a.k_cache + row0 * ROWB, static_cast<uint32_t>(nlive * ROWB));
-    const rsrc_t rv = make_rsrc(a.v_cache + row0 * ROWB, static_cast<uint32_t>(nlive * ROWB));
+    nl = uni(nl);
+    if (nl == 0) page = 0;
+    row0[blk] = uni64(cache_row(page, e.g, t0 & ps_mask, a.num_kv_heads, a.ps_log2));
+    nlive[blk] = nl;
+    rk[blk] = make_rsrc(a.k_cache + row0[blk] * ROWB, static_cast<uint32_t>(nl * ROWB));
+    rv[blk] = make_rsrc(a.v_cache + row0[blk] * ROWB, static_cast<uint32_t>(nl * ROWB));
+  }
+  // K first, then its scales, then V and its scales: the score math waits for
+  // K alone while V is still in flight.
 #pragma unroll
-    for (int i = 0; i < LPB; ++i) {
-      st.k[blk][i] = bload16(rk, lane_off + 64 * i);
-      st.v[blk][i] = bload16(rv, lane_off + 64 * i);
-    }
-    if constexpr (SM == PA_SCALE_PER_TOKEN_HEAD) {
-      const uint64_t vplane = static_cast<uint64_t>(a.num_pages) * a.num_kv_heads << a.ps_log2;
-      const rsrc_t rks = make_rsrc(a.kv_scales + row0, static_cast<uint32_t>(nlive * 4));
-      const rsrc_t rvs = make_rsrc(a.kv_scales + vplane + row0, static_cast<uint32_t>(nlive * 4));
+  for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+    for (int i = 0; i < LPB; ++i) st.k[blk][i] = bload16(rk[blk], lane_off + 64 * i);
+  if constexpr (SM == PA_SCALE_PER_TOKEN_HEAD) {
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+      const rsrc_t rks = make_rsrc(a.kv_scales + row0[blk], static_cast<uint32_t>(nlive[blk] * 4));
       st.ks[blk] = __builtin_bit_cast(f32x4, bload16(rks, 16u * j));
+    }
+  }
+#pragma unroll
+  for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+    for (int i = 0; i < LPB; ++i) st.v[blk][i] = bload16(rv[blk], lane_off + 64 * i);
+  if constexpr (SM == PA_SCALE_PER_TOKEN_HEAD) {
+    const uint64_t vplane = static_cast<uint64_t>(a.num_pages) * a.num_kv_heads << a.ps_log2;
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+      const rsrc_t rvs = make_rsrc(a.kv_scales + vplane + row0[blk], static_cast<uint32_t>(nlive[blk] * 4));
       st.vs[blk] = __builtin_bit_cast(f32x4, bload16(rvs, 16u * j));
     }
   }
@@ -262,10 +281,11 @@ __device__ __forceinline__ void load_q(const DecodeArgs& a, const Entry& e, int 
   }
 }
 
-template <int D, bool FP8, int SM, int RT, int NB, int NW>
+template <int D, bool FP8, int SM, int RT, int NB, int NW, int NS>
 __global__ __launch_bounds__(NW * 64, 1) void partition_kernel(DecodeArgs a) {
   using C = Cfg<D, FP8, RT, NB, NW>;
   constexpr int KC = C::KC, DT = C::DT, TC = C::TC, LPB = C::LPB;
+  static_assert(NS == 2 || NS == 3, "2 or 3 K/V register stages");
   // Prefetch the next segment's Q into registers when they are affordable.
   constexpr bool QPF = RT <= 2;
 
@@ -304,31 +324,50 @@ __global__ __launch_bounds__(NW * 64, 1) void partition_kernel(DecodeArgs a) {
 
   uint8_t* const wlds = lds_waves + wave * C::WBYTES;
 
-  Entry e0 = cursor_take<TC, NW>(cur, a, wave);
-  Entry e1 = cursor_take<TC, NW>(cur, a, wave);
-  Entry e2 = cursor_take<TC, NW>(cur, a, wave);
+  // The wave's chunk stream: ev[0] is computed, ev[1 .. NS-1] have K/V in
+  // flight, ev[NS .. 2NS-2] have block-table pages in flight. Pages are
+  // loaded NS-1 steps before the K/V loads that use them: vector loads
+  // retire in order, so waiting for a page then never waits for K/V loads
+  // that are still ahead of the math.
+  constexpr int NE = 2 * NS - 1;
+  Entry ev[NE];
+#pragma unroll
+  for (int k = 0; k < NE; ++k) ev[k] = cursor_take<TC, NW>(cur, a, wave);
 
   bf16x8 q[RT * KC];
   bf16x8 qn[QPF ? RT * KC : 1];
-  Stage<D, FP8, NB, SM> sA = {}, sB = {};
-  uint32_t pgX[NB], pgY[NB];
+  Stage<D, FP8, NB, SM> st[NS];
+#pragma unroll
+  for (int k = 0; k < NS; ++k) st[k] = {};
+  // pages of stream entry m live in pg[(m + 2) % NS] (NS = 3) / pg[m % 2]
+  uint32_t pg[NS][NB];
+  constexpr auto pslot = [](int m) { return ((m - 2 * NS + 2) % NS + NS) % NS; };
 
   // prologue, in the steady state's issue order (so that every later wait
-  // has the same number of younger loads on every path): pages of entry 0,
-  // Q of entry 0, pages of entry 1, K/V of entry 0
-  load_pages<NB>(a, e0, pgY);
-  if constexpr (QPF) load_q<D, FP8, RT>(a, e0, lane, qn);
-  load_pages<NB>(a, e1, pgX);
-  issue_kv<D, FP8, NB, SM>(a, e0, pgY, sA, lane);
+  // has the same number of younger loads on every path): the pages of the
+  // first NS-1 entries, Q of entry 0, then for k = 0 .. NS-2 the pages of
+  // entry NS-1+k and the K/V of entry k
+#pragma unroll
+  for (int k = 0; k < NS - 1; ++k) load_pages<NB>(a, ev[k], pg[pslot(k)]);
+  if constexpr (QPF) load_q<D, FP8, RT>(a, ev[0], lane, qn);
+#pragma unroll
+  for (int k = 0; k < NS - 1; ++k) {
+    load_pages<NB>(a, ev[NS - 1 + k], pg[pslot(NS - 1 + k)]);
+    issue_kv<D, FP8, NB, SM>(a, ev[k], pg[pslot(k)], st[k], lane);
+  }
 
   float m[RT], l[RT];
   f32x4 o[DT][RT];
 
-  // One step of a wave's pipeline. Issue order: pages of e2, Q of e1 (if it
-  // opens a segment), K/V of e1; then the math on e0, whose K/V were issued a
-  // step earlier. Every wait is on loads issued at least one step before.
-  auto step = [&](Stage<D, FP8, NB, SM>& cs, Stage<D, FP8, NB, SM>& ns, uint32_t (&pgc)[NB],
-                  uint32_t (&pgn)[NB]) {
+  // One step of a wave's pipeline, computing ev[0] from stage CUR. Issue
+  // order: pages of ev[NE-1], Q of ev[1] if it opens a segment, K/V of
+  // ev[NS-1] into the stage before CUR; then the math on ev[0], whose K/V
+  // were issued NS-1 steps earlier.
+  auto step = [&](auto cur_tag) {
+    constexpr int CUR = decltype(cur_tag)::value;
+    constexpr int ISS = (CUR + NS - 1) % NS;
+    Stage<D, FP8, NB, SM>& cs = st[CUR];
+    const Entry& e0 = ev[0];
     if (e0.first) {
       if constexpr (QPF) {
 #pragma unroll
@@ -344,11 +383,11 @@ __global__ __launch_bounds__(NW * 64, 1) void partition_kernel(DecodeArgs a) {
         for (int dt = 0; dt < DT; ++dt) o[dt][rt] = f32x4{0, 0, 0, 0};
       }
     }
-    load_pages<NB>(a, e2, pgn);
+    load_pages<NB>(a, ev[NE - 1], pg[CUR]);
     if constexpr (QPF) {
-      if (e1.live && e1.first) load_q<D, FP8, RT>(a, e1, lane, qn);
+      if (ev[1].live && ev[1].first) load_q<D, FP8, RT>(a, ev[1], lane, qn);
     }
-    issue_kv<D, FP8, NB, SM>(a, e1, pgc, ns, lane);
+    issue_kv<D, FP8, NB, SM>(a, ev[NS - 1], pg[(CUR + 1) % NS], st[ISS], lane);
 
     if (e0.data) {
       // ---- S^T = K Q^T: lane holds tokens 16 blk + 4 j + i of row 16 rt + c
@@ -559,16 +598,20 @@ __global__ __launch_bounds__(NW * 64, 1) void partition_kernel(DecodeArgs a) {
       }
     }
 
-    e0 = e1;
-    e1 = e2;
-    e2 = cursor_take<TC, NW>(cur, a, wave);
+#pragma unroll
+    for (int k = 0; k < NE - 1; ++k) ev[k] = ev[k + 1];
+    ev[NE - 1] = cursor_take<TC, NW>(cur, a, wave);
   };
 
   for (;;) {
-    step(sA, sB, pgX, pgY);
-    if (!e0.live) break;
-    step(sB, sA, pgY, pgX);
-    if (!e0.live) break;
+    step(std::integral_constant<int, 0>{});
+    if (!ev[0].live) break;
+    step(std::integral_constant<int, 1>{});
+    if (!ev[0].live) break;
+    if constexpr (NS == 3) {
+      step(std::integral_constant<int, 2>{});
+      if (!ev[0].live) break;
+    }
   }
 }
 
@@ -667,9 +710,9 @@ __global__ __launch_bounds__(64) void gather_kernel(DecodeArgs a, int row_bytes,
   }
 }
 
-template <int D, bool FP8, int SM, int RT, int NB, int NW>
+template <int D, bool FP8, int SM, int RT, int NB, int NW, int NS>
 hipError_t launch_partition_t(const DecodeArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((partition_kernel<D, FP8, SM, RT, NB, NW>), dim3(grid), dim3(NW * 64), 0, s, a);
+  hipLaunchKernelGGL((partition_kernel<D, FP8, SM, RT, NB, NW, NS>), dim3(grid), dim3(NW * 64), 0, s, a);
   return hipGetLastError();
 }
 
@@ -680,15 +723,15 @@ struct VariantEntry {
   LaunchFn fn;
 };
 
-#define PA_V(D, F, SM, RT, NB, NW) \
-  { {D, F, SM, RT, NB, NW}, launch_partition_t<D, F != 0, SM, RT, NB, NW> }
+#define PA_V(D, F, SM, RT, NB, NW, NS) \
+  { {D, F, SM, RT, NB, NW, NS}, launch_partition_t<D, F != 0, SM, RT, NB, NW, NS> }
 const VariantEntry kVariants[] = {
-    PA_V(128, 0, 0, 1, 2, 4), PA_V(128, 0, 0, 2, 2, 4), PA_V(128, 0, 0, 4, 2, 4),
-    PA_V(256, 0, 0, 1, 1, 4), PA_V(256, 0, 0, 2, 1, 4),
-    PA_V(128, 1, 1, 1, 2, 4), PA_V(128, 1, 1, 2, 2, 4), PA_V(128, 1, 1, 4, 2, 4),
-    PA_V(128, 1, 2, 1, 2, 4), PA_V(128, 1, 2, 2, 2, 4), PA_V(128, 1, 2, 4, 2, 4),
-    PA_V(256, 1, 1, 1, 1, 4), PA_V(256, 1, 1, 2, 1, 4),
-    PA_V(256, 1, 2, 1, 1, 4), PA_V(256, 1, 2, 2, 1, 4),
+    PA_V(128, 0, 0, 1, 2, 4, 3), PA_V(128, 0, 0, 2, 2, 4, 3), PA_V(128, 0, 0, 4, 2, 4, 2),
+    PA_V(256, 0, 0, 1, 1, 4, 3), PA_V(256, 0, 0, 2, 1, 4, 2),
+    PA_V(128, 1, 1, 1, 2, 4, 3), PA_V(128, 1, 1, 2, 2, 4, 3), PA_V(128, 1, 1, 4, 2, 4, 2),
+    PA_V(128, 1, 2, 1, 2, 4, 3), PA_V(128, 1, 2, 2, 2, 4, 3), PA_V(128, 1, 2, 4, 2, 4, 2),
+    PA_V(256, 1, 1, 1, 1, 4, 3), PA_V(256, 1, 1, 2, 1, 4, 2),
+    PA_V(256, 1, 2, 1, 1, 4, 3), PA_V(256, 1, 2, 2, 1, 4, 2),
 };
 #undef PA_V
 

@@ -50,17 +50,36 @@ __device__ int32_t block_exclusive_scan(int32_t v, int32_t* wsum, int32_t* total
   return before + x - v;
 }
 
-__device__ __forceinline__ int32_t wg_lo(int64_t w, int64_t N, int64_t G) {
-  return static_cast<int32_t>(w * N / G);
-}
+// floor(a / b) for 0 <= a < 2^53, 0 < b < 2^31: a double quotient, then an
+// exact integer correction (the quotient can be off by one near integers).
+// Avoids the long emulated 64-bit integer division.
+struct Div {
+  int64_t b;
+  double inv;
+  __device__ explicit Div(int64_t d) : b(d), inv(1.0 / static_cast<double>(d)) {}
+  __device__ __forceinline__ int64_t operator()(int64_t a) const {
+    int64_t q = static_cast<int64_t>(static_cast<double>(a) * inv);
+    int64_t r = a - q * b;
+    while (r < 0) { --q; r += b; }
+    while (r >= b) { ++q; r -= b; }
+    return q;
+  }
+};
 
-__device__ __forceinline__ int32_t owner(int64_t x, int64_t N, int64_t G) {
-  return static_cast<int32_t>(((x + 1) * G - 1) / N);
-}
-
-__device__ __forceinline__ int32_t seg_index(int32_t x, int32_t A, int64_t N, int64_t G) {
-  return N >= G ? owner(x, N, G) - owner(A, N, G) : x - A;
-}
+struct Sched {
+  int64_t N, G;
+  Div byG, byN;
+  __device__ Sched(int64_t n, int64_t g) : N(n), G(g), byG(g), byN(n > 0 ? n : 1) {}
+  // first item of workgroup w: floor(w N / G)
+  __device__ __forceinline__ int32_t wg_lo(int64_t w) const { return static_cast<int32_t>(byG(w * N)); }
+  // workgroup owning item x: floor(((x + 1) G - 1) / N)
+  __device__ __forceinline__ int32_t owner(int64_t x) const {
+    return static_cast<int32_t>(byN((x + 1) * G - 1));
+  }
+  __device__ __forceinline__ int32_t seg_index(int32_t x, int32_t A) const {
+    return N >= G ? owner(x) - owner(A) : x - A;
+  }
+};
 
 __device__ __forceinline__ int32_t items_of(int32_t ctx, int32_t P) { return (max(ctx, 0) + P - 1) / P; }
 
@@ -92,6 +111,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   }
   int32_t N = 0;
   const int32_t first = block_exclusive_scan(sum, wsum, &N);
+  const Sched sc(N, G);
   if (bad) {
     for (int i = tid; i <= G; i += kPlanThreads) { a.wg_begin[i] = 0; a.wg_seg_begin[i] = 0; }
     for (int i = tid; i < pairs; i += kPlanThreads) a.nseg[i] = 0;
@@ -113,7 +133,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     for (int32_t b = b_lo; b < b_hi; ++b) {
       const int32_t n = items_of(a.context_lens[b], P);
       for (int32_t g = 0; g < H; ++g, A += n) {
-        const int32_t ns = seg_index(A + n - 1, A, N, G) + 1;
+        const int32_t ns = sc.seg_index(A + n - 1, A) + 1;
         split += ns > 1 ? ns : 0;
         all += ns;
       }
@@ -130,7 +150,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       a.batch_base[b] = A;
       for (int32_t g = 0; g < H; ++g, A += n) {
         const int32_t p = b * H + g;
-        const int32_t ns = seg_index(A + n - 1, A, N, G) + 1;
+        const int32_t ns = sc.seg_index(A + n - 1, A) + 1;
         nseg_t[p] = ns;
         sbase_t[p] = run_split;
         pbase_t[p] = run_all;
@@ -151,7 +171,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __syncthreads();
 
   // 3. thread t writes items [x0, x1): each item, the segment it opens, and
-  //    the segment-range start of every workgroup whose range starts there
+  //    the segment-range start of every workgroup whose range starts there.
+  //    The owning workgroup w (and its range [lo_w, hi_w)) advances with x.
   const int32_t per_x = (N + kPlanThreads - 1) / kPlanThreads;
   const int32_t x0 = min(N, tid * per_x), x1 = min(N, x0 + per_x);
   if (x0 < x1) {
@@ -168,26 +189,33 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     int32_t p = b * H + g;
     int32_t A = base_t[b] + g * n;
     int32_t ns = nseg_t[p], sb = sbase_t[p], pb = pbase_t[p];
+    int32_t w = sc.owner(x0);
+    int32_t lo_w = sc.wg_lo(w), hi_w = sc.wg_lo(w + 1);
+    int32_t w_A = sc.owner(A);
     for (int32_t x = x0; x < x1; ++x) {
-      const int32_t j = seg_index(x, A, N, G);
+      while (x >= hi_w) {  // skips empty ranges too
+        ++w;
+        lo_w = hi_w;
+        hi_w = sc.wg_lo(w + 1);
+      }
+      if (x == A) w_A = w;
+      const int32_t j = N >= G ? w - w_A : x - A;
       Span it;
       it.pair = p;
       it.tok_begin = k * P;
       it.tok_end = min((k + 1) * P, ctx);
       it.slot = ns > 1 ? sb + j : -1;
       a.items[x] = it;
-      const int32_t w = owner(x, N, G);
-      const int32_t lo_w = wg_lo(w, N, G);
       if (x == A || x == lo_w) {
-        const int32_t last = min(A + n, wg_lo(w + 1, N, G)) - 1;
+        const int32_t last = min(A + n, hi_w) - 1;
         Span sg = it;
         sg.tok_end = min((last - A + 1) * P, ctx);
         a.segs[pb + j] = sg;
       }
       if (x == lo_w) {
         // workgroups ceil(x G / N) .. w all start their (possibly empty) range at x
-        const int32_t w0 = static_cast<int32_t>((static_cast<int64_t>(x) * G + N - 1) / N);
-        for (int32_t w2 = w0; w2 <= w; ++w2) a.wg_seg_begin[w2] = pb + j;
+        for (int32_t w2 = w; w2 >= 0 && (w2 == w || sc.wg_lo(w2) == x); --w2)
+          a.wg_seg_begin[w2] = pb + j;
       }
       if (++k == n) {  // next pair: next kv head, or the next sequence
         k = 0;
@@ -210,7 +238,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   }
 
   // 4. item ranges
-  for (int32_t w = tid; w <= G; w += kPlanThreads) a.wg_begin[w] = wg_lo(w, N, G);
+  for (int32_t w = tid; w <= G; w += kPlanThreads) a.wg_begin[w] = sc.wg_lo(w);
   if (tid == 0) {
     a.wg_seg_begin[G] = S;
     a.status[ST_BITS] = 0;
