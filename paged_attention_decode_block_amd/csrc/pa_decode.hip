@@ -47,6 +47,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kSlack = 8.f;  // lazy-rescale slack of the running max (log2 units)
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
@@ -63,14 +64,29 @@ __device__ __forceinline__ T ldu(const T* p, int64_t i) {
   return ((const __attribute__((address_space(4))) T*)(p))[i];
 }
 
-// 8 E4M3FN bytes -> 8 bf16 (exact: every finite E4M3FN value is a bf16 value).
+// 8 E4M3FN bytes -> 8 bf16, two per instruction (gfx950 scaled conversion
+// with scale 1). Exact: every finite E4M3FN value is a bf16 value.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
-  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(lo), false);
-  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(lo), true);
-  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(hi), false);
-  const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(hi), true);
-  const f32x8 f = {a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
-  return __builtin_convertvector(f, bf16x8);
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(lo), 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(lo), 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(hi), 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(hi), 1.0f, true);
+  return bf16x8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
+
+// LDS transpose read (gfx950 ds_read_b64_tr_b16). Within each 16-lane group,
+// lane i receives halfword i % 4 of the 8 bytes addressed by lane
+// 4 e + i / 4, as its element e (e = 0..3). With lane c of a group
+// addressing the 4 dims starting at 4 (c % 4) of token row r0 + c / 4 of a
+// row-major tile, lane c gets tokens r0 .. r0+3 of dim c: an MFMA operand
+// whose k index runs over tokens.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x4 lds_read_tr(const uint8_t* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(
+          (__attribute__((address_space(3))) uint8_t*)(const_cast<uint8_t*>(p))));
+  return __builtin_bit_cast(bf16x4, v);
 }
 
 template <int D, bool FP8, int RT, int NB, int NW>
@@ -81,7 +97,8 @@ struct Cfg {
   static constexpr int KC = D / 32;            // MFMA k-steps over head_dim
   static constexpr int DT = D / 16;            // 16-dim tiles of the output
   static constexpr int TC = 16 * NB;           // tokens per chunk
-  static constexpr int VROW = 2 * D + 8;       // bytes per V row in LDS (bank spread)
+  static constexpr int VROW = 2 * D + 32;      // bytes per V row in LDS: 16-B aligned rows,
+                                               // 8-dword bank shift per row
   static constexpr int VBYTES = TC * VROW;
   static constexpr int OROW = D + 4;           // floats per row of the merge tile
   static constexpr int OBYTES = 16 * OROW * 4;
@@ -434,9 +451,19 @@ __global__ __launch_bounds__(NW * 64, 1) void partition_kernel(DecodeArgs a) {
         }
         cm = fmaxf(cm, __shfl_xor(cm, 16));
         cm = fmaxf(cm, __shfl_xor(cm, 32));
-        const float mn = fmaxf(m[rt], cm);
-        const float mu = mn == neg_inf() ? 0.f : mn;
-        const float alpha = __builtin_amdgcn_exp2f(m[rt] - mu);
+        // Lazy rescale: keep the running max m while every row's chunk max
+        // stays within 2^kSlack of it (then p <= 2^kSlack, exact enough in
+        // fp32 and bf16); move it, rescaling l and O, only when some row of
+        // the wave exceeds that (a wave-uniform branch).
+        if (__builtin_amdgcn_ballot_w64(cm > m[rt] + kSlack) != 0) {
+          const float mn = fmaxf(m[rt], cm);
+          const float alpha = __builtin_amdgcn_exp2f(m[rt] - (mn == neg_inf() ? 0.f : mn));
+          l[rt] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) o[dt][rt] *= alpha;
+          m[rt] = mn;
+        }
+        const float mu = m[rt] == neg_inf() ? 0.f : m[rt];
         float ps = 0.f;
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk) {
@@ -448,10 +475,7 @@ __global__ __launch_bounds__(NW * 64, 1) void partition_kernel(DecodeArgs a) {
             else pv[blk][rt][i] = p;
           }
         }
-        l[rt] = l[rt] * alpha + ps;
-        m[rt] = mn;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[dt][rt] *= alpha;
+        l[rt] += ps;
       }
 
       // ---- V rows -> wave-private LDS tile (row-major bf16)
@@ -462,25 +486,20 @@ __global__ __launch_bounds__(NW * 64, 1) void partition_kernel(DecodeArgs a) {
         for (int i = 0; i < LPB; ++i) {
           const u32x4 wv = cs.v[blk][i];
           if constexpr (FP8) {
-            const bf16x8 lo = fp8x8_to_bf16(wv.x, wv.y);
-            const bf16x8 hi = fp8x8_to_bf16(wv.z, wv.w);
-            const u32x4 l4 = __builtin_bit_cast(u32x4, lo);
-            const u32x4 h4 = __builtin_bit_cast(u32x4, hi);
             uint8_t* dst = vrow + 128 * i + 32 * j;
-            *reinterpret_cast<u32x2*>(dst + 0) = u32x2{l4.x, l4.y};
-            *reinterpret_cast<u32x2*>(dst + 8) = u32x2{l4.z, l4.w};
-            *reinterpret_cast<u32x2*>(dst + 16) = u32x2{h4.x, h4.y};
-            *reinterpret_cast<u32x2*>(dst + 24) = u32x2{h4.z, h4.w};
+            *reinterpret_cast<bf16x8*>(dst + 0) = fp8x8_to_bf16(wv.x, wv.y);
+            *reinterpret_cast<bf16x8*>(dst + 16) = fp8x8_to_bf16(wv.z, wv.w);
           } else {
-            uint8_t* dst = vrow + 64 * i + 16 * j;
-            *reinterpret_cast<u32x2*>(dst + 0) = u32x2{wv.x, wv.y};
-            *reinterpret_cast<u32x2*>(dst + 8) = u32x2{wv.z, wv.w};
+            *reinterpret_cast<u32x4*>(vrow + 64 * i + 16 * j) = wv;
           }
         }
       }
 
-      // ---- O^T += V^T P^T (token order inside a k-step is the S^T lane order)
-      const uint16_t* vt = reinterpret_cast<const uint16_t*>(wlds) + (4 * j) * (C::VROW / 2) + c;
+      // ---- O^T += V^T P^T (token order inside a k-step is the S^T lane
+      // order). Lane (c, j) addresses token row 4 j + c / 4 (+16 per block),
+      // dims 16 dt + 4 (c % 4): the transpose read hands it tokens
+      // 4 j .. 4 j + 3 of dim 16 dt + c.
+      const uint8_t* vt = wlds + (4 * j + (c >> 2)) * C::VROW + 8 * (c & 3);
       if constexpr (NB == 1) {
         bf16x4 bp[RT];
 #pragma unroll
@@ -490,10 +509,7 @@ __global__ __launch_bounds__(NW * 64, 1) void partition_kernel(DecodeArgs a) {
         }
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          uint16_t av[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) av[i] = vt[i * (C::VROW / 2) + 16 * dt];
-          const bf16x4 A = __builtin_bit_cast(bf16x4, av);
+          const bf16x4 A = lds_read_tr(vt + 32 * dt);
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt)
             o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, bp[rt], o[dt][rt], 0, 0, 0);
@@ -514,13 +530,9 @@ __global__ __launch_bounds__(NW * 64, 1) void partition_kernel(DecodeArgs a) {
         for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
           for (int qq = 0; qq < NB / 2; ++qq) {
-            uint16_t av[8];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              av[i] = vt[(32 * qq + i) * (C::VROW / 2) + 16 * dt];
-              av[4 + i] = vt[(32 * qq + 16 + i) * (C::VROW / 2) + 16 * dt];
-            }
-            const bf16x8 A = __builtin_bit_cast(bf16x8, av);
+            const bf16x4 lo = lds_read_tr(vt + (32 * qq) * C::VROW + 32 * dt);
+            const bf16x4 hi = lds_read_tr(vt + (32 * qq + 16) * C::VROW + 32 * dt);
+            const bf16x8 A = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
               o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, bp[qq][rt], o[dt][rt], 0, 0, 0);
@@ -728,10 +740,10 @@ struct VariantEntry {
 const VariantEntry kVariants[] = {
     PA_V(128, 0, 0, 1, 2, 4, 3), PA_V(128, 0, 0, 2, 2, 4, 3), PA_V(128, 0, 0, 4, 2, 4, 2),
     PA_V(256, 0, 0, 1, 1, 4, 3), PA_V(256, 0, 0, 2, 1, 4, 2),
-    PA_V(128, 1, 1, 1, 2, 4, 3), PA_V(128, 1, 1, 2, 2, 4, 3), PA_V(128, 1, 1, 4, 2, 4, 2),
-    PA_V(128, 1, 2, 1, 2, 4, 3), PA_V(128, 1, 2, 2, 2, 4, 3), PA_V(128, 1, 2, 4, 2, 4, 2),
-    PA_V(256, 1, 1, 1, 1, 4, 3), PA_V(256, 1, 1, 2, 1, 4, 2),
-    PA_V(256, 1, 2, 1, 1, 4, 3), PA_V(256, 1, 2, 2, 1, 4, 2),
+    PA_V(128, 1, 1, 1, 4, 4, 3), PA_V(128, 1, 1, 2, 2, 4, 3), PA_V(128, 1, 1, 4, 2, 4, 2),
+    PA_V(128, 1, 2, 1, 4, 4, 3), PA_V(128, 1, 2, 2, 2, 4, 3), PA_V(128, 1, 2, 4, 2, 4, 2),
+    PA_V(256, 1, 1, 1, 2, 4, 3), PA_V(256, 1, 1, 2, 1, 4, 2),
+    PA_V(256, 1, 2, 1, 2, 4, 3), PA_V(256, 1, 2, 2, 1, 4, 2),
 };
 #undef PA_V
 
