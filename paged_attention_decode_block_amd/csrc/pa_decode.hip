@@ -18,10 +18,11 @@
 //   * the workgroup walks its segments (token ranges of one (sequence, kv
 //     head) pair); inside a segment wave w takes chunks w, w + NW, ... of
 //     TC = 16 * NB tokens
-//   * each wave runs a three-stage software pipeline over its chunk stream:
-//     block-table entries two chunks ahead (scalar loads), K/V rows one chunk
-//     ahead (16-byte vector loads straight into MFMA operand registers), and
-//     the math on the current chunk
+//   * each wave runs an NS-stage software pipeline over its chunk stream:
+//     the K/V rows of chunk i + NS - 1 (16-byte buffer loads straight into
+//     MFMA operand registers) are issued while chunk i is computed, and the
+//     block-table entries that address them were loaded NS - 1 chunks before
+//     that, so no wait for an entry ever drains the K/V loads in flight
 //   * S^T = K Q^T on MFMA 16x16x32 bf16 (K rows are the A operand as loaded;
 //     fp8 K is decoded to bf16 exactly); fp32 online softmax in the exp2
 //     domain with the causal mask of the appended tokens; O^T += V^T P^T on

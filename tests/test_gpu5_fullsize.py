@@ -1,0 +1,46 @@
+"""Full-size workloads in the launch configuration bench.py times.
+
+Every output must be finite and the device status clean; a sample of whole
+sequences (the first, the last, the longest and the one with the smallest
+partial tail) is compared with the CPU oracle element by element, each
+sequence attended on its own.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import paged_attention_decode_block_amd as pa
+import workloads as W
+from tests.gpu_util import run, say, to_f64, tol
+from tests.helpers import assert_close
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+FULL = ["C1_tiny", "C2_single_seq", "C3_batched_gqa", "C4_fp8_q1_per_token",
+        "C4_fp8_q4_per_token", "C4_fp8_q1_per_tensor", "C4_fp8_q4_per_tensor",
+        "C5_long_ctx_d256"]
+
+
+def _sample(ctx, P):
+    ctx = list(ctx)
+    picks = {0, len(ctx) - 1, int(np.argmax(ctx)),
+             min(range(len(ctx)), key=lambda b: (ctx[b] % P) or P)}
+    return sorted(picks)
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled_parity(name):
+    spec = W.CONFIGS[name]
+    w = W.generate(spec, 2026)
+    say(f"[full] {name}: {spec.batch} sequences, {int(w.context_lens.sum())} tokens")
+    out, plan = run(w)
+    assert pa.pa_plan_status(plan) == 0
+    got = to_f64(out)
+    assert np.isfinite(got).all()
+    for b in _sample(w.context_lens.tolist(), spec.partition_size):
+        want, _ = oracle.decode(w.q[b:b + 1], w.k_cache, w.v_cache, w.block_table[b:b + 1],
+                                w.context_lens[b:b + 1], spec.q_len, spec.scale, spec.page_size,
+                                spec.kv_dtype, spec.kv_scale_mode, w.kv_scales)
+        err = assert_close(got[b:b + 1], want, tol(spec), f"{name} sequence {b}")
+        say(f"[full] {name} sequence {b} (ctx {int(w.context_lens[b])}): max abs err {err:.2e}")
