@@ -11,7 +11,7 @@
 #include <mutex>
 #include <string>
 
-#include "pa_common.h"
+#include "pa_plan.h"
 
 namespace {
 
@@ -329,7 +329,7 @@ int pa_plan(const pa_dims* dims, const int32_t* context_lens, void* workspace,
   a.partition = d.partition_size;
   a.grid = L.grid;
   a.capacity = d.max_pages_per_seq * d.page_size;
-  if (int rc = hip_check(pa::launch_plan(a, static_cast<hipStream_t>(stream)), "plan launch"))
+  if (int rc = hip_check(pa::launch_plan(a, L.max_items, static_cast<hipStream_t>(stream)), "plan launch"))
     return rc;
   *plan = p;
   return ok();

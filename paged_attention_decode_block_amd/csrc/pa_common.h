@@ -19,21 +19,6 @@ struct Span {
 // Device status word layout in the workspace (int32[4]).
 enum { ST_BITS = 0, ST_ITEMS = 1, ST_SEGS = 2 };
 
-struct PlanArgs {
-  const int32_t* context_lens;
-  int32_t* status;
-  int32_t* wg_begin;
-  int32_t* wg_seg_begin;
-  Span* items;
-  Span* segs;
-  int32_t* nseg;
-  int32_t* seg_base;
-  int32_t* pseg_base;
-  int32_t* batch_base;
-  int32_t batch, num_kv_heads, q_len, partition, grid;
-  int32_t capacity;  // max_pages_per_seq * page_size
-};
-
 struct DecodeArgs {
   const uint16_t* q;            // bf16 bits [B, q_len, Hq, D]
   const uint8_t* k_cache;       // [num_pages, Hkv, ps, D] elements
@@ -86,7 +71,6 @@ const Variant& variant(int i);
 // rows per kv head), or -1.
 int pick_variant(int head_dim, int fp8, int scale_mode, int rows);
 
-hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_partition(int variant, const DecodeArgs& a, int grid, hipStream_t s);
 hipError_t launch_reduce(const DecodeArgs& a, int head_dim, int num_pairs, hipStream_t s);
 hipError_t launch_gather(const DecodeArgs& a, int head_dim, int elt_bytes, int capacity,

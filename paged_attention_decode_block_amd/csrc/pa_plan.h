@@ -1,0 +1,28 @@
+// Internal declarations of the work-list builder (pa_plan.hip), used by the
+// C-ABI wrappers. gfx950 (CDNA4) only.
+#pragma once
+
+#include "pa_common.h"
+
+namespace pa {
+
+struct PlanArgs {
+  const int32_t* context_lens;
+  int32_t* status;
+  int32_t* wg_begin;
+  int32_t* wg_seg_begin;
+  Span* items;
+  Span* segs;
+  int32_t* nseg;
+  int32_t* seg_base;
+  int32_t* pseg_base;
+  int32_t* batch_base;
+  int32_t batch, num_kv_heads, q_len, partition, grid;
+  int32_t capacity;  // max_pages_per_seq * page_size
+};
+
+// Launches the plan kernel on s; max_items bounds the item count (it sizes
+// the grid).
+hipError_t launch_plan(const PlanArgs& a, int64_t max_items, hipStream_t s);
+
+}  // namespace pa

@@ -8,60 +8,79 @@
 // ranges per workgroup, segments = same-pair runs inside a range, partial
 // slots only for pairs split over several workgroups.
 //
-// Method: prefix sums (items per sequence, segments per pair, both owned by
-// thread chunks) and a closed form per item; each thread writes a contiguous
-// run of items. With N items over G workgroups, workgroup w starts at
-// lo(w) = floor(w N / G) and item x belongs to owner(x) = floor(((x+1) G - 1) / N),
-// the largest w with lo(w) <= x. When N >= G every range is non-empty, so
-// the segment index of item x inside its pair (first item A) is
-// owner(x) - owner(A); when N < G every non-empty range holds one item and the
-// index is x - A. Item x starts a segment when x == A or x == lo(owner(x)).
-#include "pa_common.h"
+// Method: prefix sums (items per sequence, then split slots and segments per
+// pair) and a closed form per item. With N items over G workgroups,
+// workgroup w starts at lo(w) = floor(w N / G) and item x belongs to
+// owner(x) = floor(((x+1) G - 1) / N), the largest w with lo(w) <= x. When
+// N >= G every range is non-empty, so the segment index of item x inside its
+// pair (first item A) is owner(x) - owner(A); when N < G every non-empty range
+// holds one item and the index is x - A. Item x starts a segment when x == A
+// or x == lo(owner(x)); a workgroup's first segment is the one that holds item
+// lo(w), so empty ranges need no special case.
+//
+// Latency is the whole cost of this kernel, so: the per-sequence and per-pair
+// tables live in LDS whenever they fit (typed LDS accesses, which never wait
+// on outstanding global stores), every global store sits after the loads of
+// its phase, and divisions go through a double reciprocal with one exact
+// correction instead of the emulated 64-bit integer division. When the tables
+// fit in LDS, several workgroups run: each recomputes the (small) tables in
+// its own LDS and writes only its slice of the items, ranges and tables, so
+// the item writes are spread over several CUs with no inter-workgroup
+// synchronisation. Otherwise one workgroup keeps the tables in the workspace.
+#include "pa_plan.h"
 
 namespace pa {
 namespace {
 
-constexpr int kPlanThreads = 1024;
+constexpr int kPlanThreads = 512;
 constexpr int kPlanWaves = kPlanThreads / 64;
-constexpr int kLdsSeqs = 4096;   // sequences whose item bases are kept in LDS
-constexpr int kLdsPairs = 4096;  // pairs whose segment counts / bases are kept in LDS
+constexpr int kLdsSeqs = 4096;   // sequences whose tables fit in LDS
+constexpr int kLdsPairs = 4096;  // pairs whose tables fit in LDS
+constexpr int kPlanMaxBlocks = 64;
 
-// Exclusive prefix sum of one value per thread over the workgroup: a wave
-// scan with lane shuffles, then the 16 wave totals through LDS.
-__device__ int32_t block_exclusive_scan(int32_t v, int32_t* wsum, int32_t* total) {
+// Exclusive prefix sums of two values per thread over the workgroup: wave
+// scans with lane shuffles, then the wave totals through LDS.
+__device__ int2 block_exclusive_scan2(int2 v, int2* wsum, int2* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int32_t x = v;
+  int2 x = v;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const int32_t y = __shfl_up(x, off);
-    if (lane >= off) x += y;
+    const int yx = __shfl_up(x.x, off), yy = __shfl_up(x.y, off);
+    if (lane >= off) {
+      x.x += yx;
+      x.y += yy;
+    }
   }
   if (lane == 63) wsum[wave] = x;
   __syncthreads();
-  int32_t before = 0, tot = 0;
+  int2 before = make_int2(0, 0), tot = make_int2(0, 0);
 #pragma unroll
   for (int w = 0; w < kPlanWaves; ++w) {
-    const int32_t s = wsum[w];
-    tot += s;
-    before += w < wave ? s : 0;
+    const int2 s = wsum[w];
+    tot.x += s.x;
+    tot.y += s.y;
+    if (w < wave) {
+      before.x += s.x;
+      before.y += s.y;
+    }
   }
   *total = tot;
   __syncthreads();
-  return before + x - v;
+  return make_int2(before.x + x.x - v.x, before.y + x.y - v.y);
 }
 
-// floor(a / b) for 0 <= a < 2^53, 0 < b < 2^31: a double quotient, then an
-// exact integer correction (the quotient can be off by one near integers).
-// Avoids the long emulated 64-bit integer division.
+// floor(a / b) for 0 <= a < 2^53 and 0 < b < 2^31 when the quotient is below
+// 2^31: the double product a * (1/b) is within 2^-21 of a / b, so its
+// truncation is off by at most one, which one exact remainder test fixes.
 struct Div {
   int64_t b;
   double inv;
   __device__ explicit Div(int64_t d) : b(d), inv(1.0 / static_cast<double>(d)) {}
-  __device__ __forceinline__ int64_t operator()(int64_t a) const {
-    int64_t q = static_cast<int64_t>(static_cast<double>(a) * inv);
-    int64_t r = a - q * b;
-    while (r < 0) { --q; r += b; }
-    while (r >= b) { ++q; r -= b; }
+  __device__ __forceinline__ int32_t operator()(int64_t a) const {
+    int32_t q = static_cast<int32_t>(static_cast<double>(a) * inv);
+    const int64_t r = a - static_cast<int64_t>(q) * b;
+    q += (r >= b) ? 1 : 0;
+    q -= (r < 0) ? 1 : 0;
     return q;
   }
 };
@@ -71,124 +90,153 @@ struct Sched {
   Div byG, byN;
   __device__ Sched(int64_t n, int64_t g) : N(n), G(g), byG(g), byN(n > 0 ? n : 1) {}
   // first item of workgroup w: floor(w N / G)
-  __device__ __forceinline__ int32_t wg_lo(int64_t w) const { return static_cast<int32_t>(byG(w * N)); }
+  __device__ __forceinline__ int32_t wg_lo(int64_t w) const { return byG(w * N); }
   // workgroup owning item x: floor(((x + 1) G - 1) / N)
-  __device__ __forceinline__ int32_t owner(int64_t x) const {
-    return static_cast<int32_t>(byN((x + 1) * G - 1));
-  }
+  __device__ __forceinline__ int32_t owner(int64_t x) const { return byN((x + 1) * G - 1); }
   __device__ __forceinline__ int32_t seg_index(int32_t x, int32_t A) const {
     return N >= G ? owner(x) - owner(A) : x - A;
   }
 };
 
-__device__ __forceinline__ int32_t items_of(int32_t ctx, int32_t P) { return (max(ctx, 0) + P - 1) / P; }
+// Per-sequence and per-pair tables: LDS arrays when they fit (kLds), else
+// the workspace arrays of the same meaning (context lengths are then reread
+// from the input).
+template <bool kLds>
+struct Tables {
+  int32_t* ctx;    // [B]      context length (LDS only)
+  int32_t* base;   // [B + 1]  first item of each sequence
+  int32_t* nseg;   // [pairs]
+  int32_t* sbase;  // [pairs]  first split slot
+  int32_t* pbase;  // [pairs]  first segment
+  const int32_t* in_ctx;
+  __device__ __forceinline__ int32_t context(int32_t b) const {
+    if constexpr (kLds) return ctx[b];
+    return in_ctx[b];
+  }
+};
 
+template <bool kLds>
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
-  __shared__ int32_t wsum[kPlanWaves];
+  constexpr int NS = kLds ? kLdsSeqs : 1, NP = kLds ? kLdsPairs : 1;
+  __shared__ int2 wsum[kPlanWaves];
   __shared__ int32_t bad;
-  __shared__ int32_t l_base[kLdsSeqs + 1];
-  __shared__ int32_t l_nseg[kLdsPairs], l_sbase[kLdsPairs], l_pbase[kLdsPairs];
+  __shared__ int32_t l_ctx[NS], l_base[NS + 1];
+  __shared__ int32_t l_nseg[NP], l_sbase[NP], l_pbase[NP];
   const int tid = threadIdx.x;
+  // this block's share of the per-item, per-workgroup and per-table writes
+  const int32_t nblk = kLds ? static_cast<int32_t>(gridDim.x) : 1;
+  const int32_t blk = kLds ? static_cast<int32_t>(blockIdx.x) : 0;
+  const int32_t gtid = blk * kPlanThreads + tid, gstride = nblk * kPlanThreads;
   const int32_t B = a.batch, H = a.num_kv_heads, P = a.partition, G = a.grid;
   const int32_t pairs = B * H;
-  // per-sequence / per-pair tables: LDS when they fit, else the workspace
-  int32_t* base_t = B < kLdsSeqs ? l_base : a.batch_base;
-  int32_t* nseg_t = pairs <= kLdsPairs ? l_nseg : a.nseg;
-  int32_t* sbase_t = pairs <= kLdsPairs ? l_sbase : a.seg_base;
-  int32_t* pbase_t = pairs <= kLdsPairs ? l_pbase : a.pseg_base;
+  Tables<kLds> t;
+  if constexpr (kLds) {
+    t = {l_ctx, l_base, l_nseg, l_sbase, l_pbase, a.context_lens};
+  } else {
+    t = {nullptr, a.batch_base, a.nseg, a.seg_base, a.pseg_base, a.context_lens};
+  }
+  const Div byP(P), byH(H);
+  auto items_of = [&](int32_t ctx) { return byP(static_cast<int64_t>(ctx) + P - 1); };
   if (tid == 0) bad = 0;
-  __syncthreads();
 
-  // 1. thread t owns sequences [b_lo, b_hi): validate, count items, and
-  //    find the first item of each by a prefix sum
+  // 1. thread t owns sequences [b_lo, b_hi): validate, count items; the
+  //    first item of each sequence comes from a prefix sum
   const int32_t per_b = (B + kPlanThreads - 1) / kPlanThreads;
   const int32_t b_lo = min(B, tid * per_b), b_hi = min(B, b_lo + per_b);
   int32_t sum = 0;
+  bool my_bad = false;
   for (int32_t b = b_lo; b < b_hi; ++b) {
     const int32_t c = a.context_lens[b];
-    if (c < max(1, a.q_len) || c > a.capacity) atomicOr(&bad, 1);
-    sum += H * items_of(c, P);
+    const bool ok = c >= max(1, a.q_len) && c <= a.capacity;
+    my_bad |= !ok;
+    if constexpr (kLds) t.ctx[b] = c;
+    sum += ok ? H * items_of(c) : 0;
   }
-  int32_t N = 0;
-  const int32_t first = block_exclusive_scan(sum, wsum, &N);
-  const Sched sc(N, G);
+  __syncthreads();  // bad = 0 is visible
+  if (my_bad) bad = 1;
+  int2 tot;
+  const int32_t first = block_exclusive_scan2(make_int2(sum, 0), wsum, &tot).x;
+  const int32_t N = tot.x;
   if (bad) {
-    for (int i = tid; i <= G; i += kPlanThreads) { a.wg_begin[i] = 0; a.wg_seg_begin[i] = 0; }
-    for (int i = tid; i < pairs; i += kPlanThreads) a.nseg[i] = 0;
-    for (int i = tid; i <= pairs; i += kPlanThreads) { a.seg_base[i] = 0; a.pseg_base[i] = 0; }
-    for (int i = tid; i <= B; i += kPlanThreads) a.batch_base[i] = 0;
-    if (tid == 0) {
+    for (int i = gtid; i <= G; i += gstride) { a.wg_begin[i] = 0; a.wg_seg_begin[i] = 0; }
+    for (int i = gtid; i < pairs; i += gstride) a.nseg[i] = 0;
+    for (int i = gtid; i <= pairs; i += gstride) { a.seg_base[i] = 0; a.pseg_base[i] = 0; }
+    for (int i = gtid; i <= B; i += gstride) a.batch_base[i] = 0;
+    if (gtid == 0) {
       a.status[ST_BITS] = PA_DEV_BAD_CONTEXT;
       a.status[ST_ITEMS] = 0;
       a.status[ST_SEGS] = 0;
     }
     return;
   }
-
-  // 2. the same thread's pairs: segment counts, then slot bases (split pairs
-  //    only) and segment bases by two more prefix sums
-  int32_t split = 0, all = 0;
+  const Sched sc(N, G);
   {
     int32_t A = first;
     for (int32_t b = b_lo; b < b_hi; ++b) {
-      const int32_t n = items_of(a.context_lens[b], P);
-      for (int32_t g = 0; g < H; ++g, A += n) {
-        const int32_t ns = sc.seg_index(A + n - 1, A) + 1;
-        split += ns > 1 ? ns : 0;
-        all += ns;
-      }
+      t.base[b] = A;
+      A += H * items_of(t.context(b));
     }
-  }
-  int32_t slots = 0, S = 0;
-  int32_t run_split = block_exclusive_scan(split, wsum, &slots);
-  int32_t run_all = block_exclusive_scan(all, wsum, &S);
-  {
-    int32_t A = first;
-    for (int32_t b = b_lo; b < b_hi; ++b) {
-      const int32_t n = items_of(a.context_lens[b], P);
-      base_t[b] = A;
-      a.batch_base[b] = A;
-      for (int32_t g = 0; g < H; ++g, A += n) {
-        const int32_t p = b * H + g;
-        const int32_t ns = sc.seg_index(A + n - 1, A) + 1;
-        nseg_t[p] = ns;
-        sbase_t[p] = run_split;
-        pbase_t[p] = run_all;
-        a.nseg[p] = ns;
-        a.seg_base[p] = run_split;
-        a.pseg_base[p] = run_all;
-        run_split += ns > 1 ? ns : 0;
-        run_all += ns;
-      }
-    }
-  }
-  if (tid == 0) {
-    base_t[B] = N;
-    a.batch_base[B] = N;
-    a.seg_base[pairs] = slots;
-    a.pseg_base[pairs] = S;
+    if (tid == 0) t.base[B] = N;
   }
   __syncthreads();
 
-  // 3. thread t writes items [x0, x1): each item, the segment it opens, and
-  //    the segment-range start of every workgroup whose range starts there.
-  //    The owning workgroup w (and its range [lo_w, hi_w)) advances with x.
-  const int32_t per_x = (N + kPlanThreads - 1) / kPlanThreads;
-  const int32_t x0 = min(N, tid * per_x), x1 = min(N, x0 + per_x);
+  // 2. thread t owns pairs [p_lo, p_hi): segment counts, then split-slot and
+  //    segment bases by a prefix sum
+  const int32_t per_p = (pairs + kPlanThreads - 1) / kPlanThreads;
+  const int32_t p_lo = min(pairs, tid * per_p), p_hi = min(pairs, p_lo + per_p);
+  int2 cnt = make_int2(0, 0);  // (split slots, segments)
+  if (p_lo < p_hi) {
+    int32_t b = byH(p_lo), g = p_lo - b * H;
+    int32_t n = items_of(t.context(b));
+    for (int32_t p = p_lo; p < p_hi; ++p) {
+      const int32_t A = t.base[b] + g * n;
+      const int32_t ns = sc.seg_index(A + n - 1, A) + 1;
+      t.nseg[p] = ns;
+      cnt.x += ns > 1 ? ns : 0;
+      cnt.y += ns;
+      if (++g == H && p + 1 < p_hi) {
+        g = 0;
+        n = items_of(t.context(++b));
+      }
+    }
+  }
+  const int2 run0 = block_exclusive_scan2(cnt, wsum, &tot);
+  const int32_t slots = tot.x, S = tot.y;
+  {
+    int2 run = run0;
+    for (int32_t p = p_lo; p < p_hi; ++p) {
+      const int32_t ns = t.nseg[p];
+      t.sbase[p] = run.x;
+      t.pbase[p] = run.y;
+      run.x += ns > 1 ? ns : 0;
+      run.y += ns;
+    }
+  }
+  __syncthreads();
+
+  // 3. this block's items [X0, X1); thread t writes the run [x0, x1) of them:
+  //    each item and the segment it opens. The owning workgroup w (and its
+  //    range [lo_w, hi_w)) advances with x.
+  const Div byBlk(nblk);
+  const int32_t X0 = byBlk(static_cast<int64_t>(blk) * N);
+  const int32_t X1 = byBlk(static_cast<int64_t>(blk + 1) * N);
+  const int32_t per_x = (X1 - X0 + kPlanThreads - 1) / kPlanThreads;
+  const int32_t x0 = min(X1, X0 + tid * per_x), x1 = min(X1, x0 + per_x);
   if (x0 < x1) {
-    int lo = 0, hi = B;  // largest b with base_t[b] <= x0
+    int lo = 0, hi = B;  // largest b with base[b] <= x0
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (base_t[mid] <= x0) lo = mid; else hi = mid;
+      if (t.base[mid] <= x0) lo = mid; else hi = mid;
     }
     int32_t b = lo;
-    int32_t ctx = a.context_lens[b];
-    int32_t n = items_of(ctx, P);
-    int32_t g = (x0 - base_t[b]) / n;
-    int32_t k = x0 - base_t[b] - g * n;
+    int32_t ctx = t.context(b);
+    int32_t n = items_of(ctx);
+    const int32_t bb = t.base[b];
+    int32_t g = Div(n)(x0 - bb);
+    int32_t k = x0 - bb - g * n;
     int32_t p = b * H + g;
-    int32_t A = base_t[b] + g * n;
-    int32_t ns = nseg_t[p], sb = sbase_t[p], pb = pbase_t[p];
+    int32_t A = bb + g * n;
+    int32_t ns = t.nseg[p], sb = t.sbase[p], pb = t.pbase[p];
     int32_t w = sc.owner(x0);
     int32_t lo_w = sc.wg_lo(w), hi_w = sc.wg_lo(w + 1);
     int32_t w_A = sc.owner(A);
@@ -205,42 +253,62 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       it.tok_begin = k * P;
       it.tok_end = min((k + 1) * P, ctx);
       it.slot = ns > 1 ? sb + j : -1;
-      a.items[x] = it;
       if (x == A || x == lo_w) {
         const int32_t last = min(A + n, hi_w) - 1;
         Span sg = it;
         sg.tok_end = min((last - A + 1) * P, ctx);
         a.segs[pb + j] = sg;
       }
-      if (x == lo_w) {
-        // workgroups ceil(x G / N) .. w all start their (possibly empty) range at x
-        for (int32_t w2 = w; w2 >= 0 && (w2 == w || sc.wg_lo(w2) == x); --w2)
-          a.wg_seg_begin[w2] = pb + j;
-      }
-      if (++k == n) {  // next pair: next kv head, or the next sequence
+      a.items[x] = it;
+      if (++k == n && x + 1 < x1) {  // next pair: next kv head, or the next sequence
         k = 0;
         A += n;
         if (++g == H) {
           g = 0;
-          if (++b < B) {
-            ctx = a.context_lens[b];
-            n = items_of(ctx, P);
-          }
+          ++b;
+          ctx = t.context(b);
+          n = items_of(ctx);
         }
         p = b * H + g;
-        if (x + 1 < x1) {
-          ns = nseg_t[p];
-          sb = sbase_t[p];
-          pb = pbase_t[p];
-        }
+        ns = t.nseg[p];
+        sb = t.sbase[p];
+        pb = t.pbase[p];
       }
     }
   }
 
-  // 4. item ranges
-  for (int32_t w = tid; w <= G; w += kPlanThreads) a.wg_begin[w] = sc.wg_lo(w);
-  if (tid == 0) {
-    a.wg_seg_begin[G] = S;
+  // 4. per workgroup: its item range and its first segment, the one holding
+  //    item lo(w) (found from the sequence and pair tables)
+  for (int32_t w = gtid; w <= G; w += gstride) {
+    const int32_t x = sc.wg_lo(w);
+    int32_t first_seg = S;
+    if (w < G) {
+      int lo = 0, hi = B;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (t.base[mid] <= x) lo = mid; else hi = mid;
+      }
+      const int32_t n = items_of(t.context(lo));
+      const int32_t g = Div(n)(x - t.base[lo]);
+      const int32_t A = t.base[lo] + g * n;
+      first_seg = t.pbase[lo * H + g] + sc.seg_index(x, A);
+    }
+    a.wg_begin[w] = x;
+    a.wg_seg_begin[w] = first_seg;
+  }
+
+  // 5. tables the decode and the tests read, copied out of LDS
+  if constexpr (kLds) {
+    for (int32_t b = gtid; b <= B; b += gstride) a.batch_base[b] = t.base[b];
+    for (int32_t p = gtid; p < pairs; p += gstride) {
+      a.nseg[p] = t.nseg[p];
+      a.seg_base[p] = t.sbase[p];
+      a.pseg_base[p] = t.pbase[p];
+    }
+  }
+  if (gtid == 0) {
+    a.seg_base[pairs] = slots;
+    a.pseg_base[pairs] = S;
     a.status[ST_BITS] = 0;
     a.status[ST_ITEMS] = N;
     a.status[ST_SEGS] = S;
@@ -249,8 +317,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
 
 }  // namespace
 
-hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, a);
+hipError_t launch_plan(const PlanArgs& a, int64_t max_items, hipStream_t s) {
+  if (a.batch <= kLdsSeqs && static_cast<int64_t>(a.batch) * a.num_kv_heads <= kLdsPairs) {
+    // about two items per thread at the largest possible item count
+    const int64_t want = (max_items + 2 * kPlanThreads - 1) / (2 * kPlanThreads);
+    const int blocks = static_cast<int>(want < 1 ? 1 : (want > kPlanMaxBlocks ? kPlanMaxBlocks : want));
+    hipLaunchKernelGGL(plan_kernel<true>, dim3(blocks), dim3(kPlanThreads), 0, s, a);
+  } else
+    hipLaunchKernelGGL(plan_kernel<false>, dim3(1), dim3(kPlanThreads), 0, s, a);
   return hipGetLastError();
 }
 
