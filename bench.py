@@ -7,10 +7,14 @@ seeded synthetic workloads (workloads.CONFIGS) already resident in HBM; before
 every step a 1 GiB read (a reduction over a scratch tensor) evicts L2 and the
 256 MB Infinity Cache, outside the timed events, so KV really streams from
 HBM. The flush reads rather than writes: a write flush would leave up to
-256 MB of dirty lines whose write-back competes with the timed kernel. HIP events on the launch stream
-bracket the plan, the partition kernel and the reduce of every step (the
-method of Ascend/RecSDK issue #1281, section "测试方法": warmups, then
-samples, median).
+256 MB of dirty lines whose write-back competes with the timed kernel.
+
+Three timed passes, each of warmups-then-samples with the median reported
+(the method of Ascend/RecSDK issue #1281, section "测试方法"): HIP events on
+the launch stream around the whole step (the headline: nothing else between
+them), around pa_decode with its plan built beforehand (decode latency), and
+around each of the three kernels (the breakdown and the partition kernel's
+roofline; these extra events cost a few microseconds of their own).
 
 The JSON line's `value` is KV-read GB/s of the whole step on the headline
 workload (batched GQA decode); `per_config` carries every workload; `roofline`
@@ -154,43 +158,77 @@ def main():
         out = torch.empty_like(d["q"])
         stream = torch.cuda.current_stream()
 
-        def step(evs=None):
-            if evs:
-                evs[0].record(stream)
-            plan = pa.pa_plan(dims, d["context_lens"], workspace=ws, stream=stream)
-            if evs:
-                evs[1].record(stream)
+        def plan_call():
+            return pa.pa_plan(dims, d["context_lens"], workspace=ws, stream=stream)
+
+        def partition_call(plan):
             pa.pa_decode_partition(plan, d["q"], d["k_cache"], d["v_cache"], d["block_table"],
                                    d["context_lens"], spec.q_len, spec.scale, mode,
                                    d["kv_scales"], out, stream=stream)
-            if evs:
-                evs[2].record(stream)
+
+        def reduce_call(plan):
             pa.pa_decode_reduce(plan, spec.q_len, mode, out, stream=stream)
-            if evs:
-                evs[3].record(stream)
-            return plan
+
+        def decode_call(plan):
+            pa.pa_decode(plan, d["q"], d["k_cache"], d["v_cache"], d["block_table"],
+                         d["context_lens"], spec.q_len, spec.scale, mode, d["kv_scales"], out,
+                         stream=stream)
+
+        def timed(body, n_events):
+            """args.steps samples of body(events), each after a cache flush;
+            returns the events of every sample."""
+            evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_events)]
+                   for _ in range(args.steps)]
+            torch.cuda.synchronize()
+            for i in range(args.steps):
+                if flush is not None:
+                    flush()
+                body(evs[i])
+            torch.cuda.synchronize()
+            return evs
+
+        def whole_step(ev):
+            ev[0].record(stream)
+            decode_call(plan_call())
+            ev[1].record(stream)
+
+        def decode_only(ev):
+            plan = plan_call()
+            ev[0].record(stream)
+            decode_call(plan)
+            ev[1].record(stream)
+
+        def per_kernel(ev):
+            ev[0].record(stream)
+            plan = plan_call()
+            ev[1].record(stream)
+            partition_call(plan)
+            ev[2].record(stream)
+            reduce_call(plan)
+            ev[3].record(stream)
 
         for _ in range(args.warmup):
             if flush is not None:
                 flush()
-            step()
+            decode_call(plan_call())
         torch.cuda.synchronize()
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-        torch.cuda.synchronize()
+        # 1. the step alone between two events (the headline); 2. the decode
+        # with its plan built before the first event; 3. events around every
+        # kernel (they add a few microseconds of their own to a step)
         t_wall = time.perf_counter()
-        for i in range(args.steps):
-            if flush is not None:
-                flush()
-            plan = step(evs[i])
-        torch.cuda.synchronize()
+        ev_step = timed(whole_step, 2)
         wall = time.perf_counter() - t_wall
+        ev_dec = timed(decode_only, 2)
+        ev_k = timed(per_kernel, 4)
+        plan = plan_call()
         status = pa.pa_plan_status(plan)
         assert status == 0, f"{name}: device status {status}"
-        plan_us = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]
-        part_us = [e[1].elapsed_time(e[2]) * 1e3 for e in evs]
-        red_us = [e[2].elapsed_time(e[3]) * 1e3 for e in evs]
-        step_us = [e[0].elapsed_time(e[3]) * 1e3 for e in evs]
-        dec_us = [e[1].elapsed_time(e[3]) * 1e3 for e in evs]
+        ms = lambda a, b: a.elapsed_time(b) * 1e3  # noqa: E731
+        step_us = [ms(e[0], e[1]) for e in ev_step]
+        dec_us = [ms(e[0], e[1]) for e in ev_dec]
+        plan_us = [ms(e[0], e[1]) for e in ev_k]
+        part_us = [ms(e[1], e[2]) for e in ev_k]
+        red_us = [ms(e[2], e[3]) for e in ev_k]
         kvb = w.kv_bytes()
         med = statistics.median
         r = {
@@ -200,6 +238,8 @@ def main():
             "partition_us_mean": statistics.fmean(part_us),
             "step_us_p10": float(np.percentile(step_us, 10)),
             "step_us_p90": float(np.percentile(step_us, 90)),
+            "decode_us_p10": float(np.percentile(dec_us, 10)),
+            "decode_us_p90": float(np.percentile(dec_us, 90)),
             "wall_us_per_step_incl_flush": wall / args.steps * 1e6,
             "step_GBps": kvb / med(step_us) / 1e3,
             "decode_GBps": kvb / med(dec_us) / 1e3,
@@ -248,9 +288,9 @@ def main():
             "latency_us": hr["step_us"],
             "decode_latency_us": hr["decode_us"],
             "frac_of_hbm_peak": round(hr["step_frac_of_peak"], 4),
-            "timing": "median of HIP-event step times (plan + partition + reduce) on the launch "
-                      "stream; 1 GiB read flush of L2 / Infinity Cache before each step, outside "
-                      "the events",
+            "timing": "median of HIP-event step times (plan + partition + reduce, two events "
+                      "per step) on the launch stream; 1 GiB read flush of L2 / Infinity Cache "
+                      "before each step, outside the events",
         },
         "roofline": {
             "bound": "hbm",
