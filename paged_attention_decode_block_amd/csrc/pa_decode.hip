@@ -76,6 +76,20 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
   return bf16x8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
+// Lane i of each lane quad's value, to every lane of the quad (DPP
+// quad_perm [i, i, i, i]).
+__device__ __forceinline__ float quad_bcast(float x, int i) {
+  const int v = __builtin_bit_cast(int, x);
+  int r;
+  switch (i) {
+    case 0: r = __builtin_amdgcn_mov_dpp(v, 0x00, 0xF, 0xF, true); break;
+    case 1: r = __builtin_amdgcn_mov_dpp(v, 0x55, 0xF, 0xF, true); break;
+    case 2: r = __builtin_amdgcn_mov_dpp(v, 0xAA, 0xF, 0xF, true); break;
+    default: r = __builtin_amdgcn_mov_dpp(v, 0xFF, 0xF, 0xF, true); break;
+  }
+  return __builtin_bit_cast(float, r);
+}
+
 // LDS transpose read (gfx950 ds_read_b64_tr_b16). Within each 16-lane group,
 // lane i receives halfword i % 4 of the 8 bytes addressed by lane
 // 4 e + i / 4, as its element e (e = 0..3). With lane c of a group
@@ -149,8 +163,10 @@ struct Stage {
   static constexpr int NS = SM == PA_SCALE_PER_TOKEN_HEAD ? NB : 1;
   u32x4 k[NB][LPB];
   u32x4 v[NB][LPB];
-  f32x4 ks[NS];  // per-token K scales of the lane's S^T tokens
-  f32x4 vs[NS];
+  // per-token scales: lane (c, j) holds those of token 4 j + c % 4 of each
+  // block; the four tokens of its S^T column come from its lane quad
+  float ks[NS];
+  float vs[NS];
 };
 
 // One entry of a wave's chunk stream (wave-uniform values).
@@ -261,7 +277,7 @@ __device__ __forceinline__ void issue_kv(const DecodeArgs& a, const Entry& e, co
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk) {
       const rsrc_t rks = make_rsrc(a.kv_scales + row0[blk], static_cast<uint32_t>(nlive[blk] * 4));
-      st.ks[blk] = __builtin_bit_cast(f32x4, bload16(rks, 16u * j));
+      st.ks[blk] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rks, 4u * (4 * j + (c & 3)), 0, 0));
     }
   }
 #pragma unroll
@@ -273,7 +289,7 @@ __device__ __forceinline__ void issue_kv(const DecodeArgs& a, const Entry& e, co
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk) {
       const rsrc_t rvs = make_rsrc(a.kv_scales + vplane + row0[blk], static_cast<uint32_t>(nlive[blk] * 4));
-      st.vs[blk] = __builtin_bit_cast(f32x4, bload16(rvs, 16u * j));
+      st.vs[blk] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rvs, 4u * (4 * j + (c & 3)), 0, 0));
     }
   }
 }
@@ -300,12 +316,12 @@ __device__ __forceinline__ void load_q(const DecodeArgs& a, const Entry& e, int 
 }
 
 template <int D, bool FP8, int SM, int RT, int NB, int NW, int NS>
-__global__ __launch_bounds__(NW * 64, 1) void partition_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(DecodeArgs a) {
   using C = Cfg<D, FP8, RT, NB, NW>;
   constexpr int KC = C::KC, DT = C::DT, TC = C::TC, LPB = C::LPB;
   static_assert(NS == 2 || NS == 3, "2 or 3 K/V register stages");
   // Prefetch the next segment's Q into registers when they are affordable.
-  constexpr bool QPF = RT <= 2;
+  constexpr bool QPF = RT == 1 || (RT == 2 && NW <= 4);
 
   __shared__ __attribute__((aligned(16))) uint8_t lds_waves[NW * C::WBYTES];
   __shared__ float st_m[NW][RT * 16];
@@ -444,7 +460,7 @@ __global__ __launch_bounds__(NW * 64, 1) void partition_kernel(DecodeArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             float v = s[blk][rt][i] * qk_f;
-            if constexpr (per_tok) v *= cs.ks[blk][i];
+            if constexpr (per_tok) v *= quad_bcast(cs.ks[blk], i);
             if (!full) v = (e0.tc0 + 16 * blk + 4 * j + i <= lim) ? v : neg_inf();
             x[blk][i] = v;
             cm = fmaxf(cm, v);
@@ -472,7 +488,7 @@ __global__ __launch_bounds__(NW * 64, 1) void partition_kernel(DecodeArgs a) {
           for (int i = 0; i < 4; ++i) {
             const float p = __builtin_amdgcn_exp2f(x[blk][i] - mu);
             ps += p;
-            if constexpr (per_tok) pv[blk][rt][i] = p * cs.vs[blk][i];
+            if constexpr (per_tok) pv[blk][rt][i] = p * quad_bcast(cs.vs[blk], i);
             else pv[blk][rt][i] = p;
           }
         }
@@ -741,8 +757,8 @@ struct VariantEntry {
 const VariantEntry kVariants[] = {
     PA_V(128, 0, 0, 1, 2, 4, 3), PA_V(128, 0, 0, 2, 2, 4, 3), PA_V(128, 0, 0, 4, 2, 4, 2),
     PA_V(256, 0, 0, 1, 1, 4, 3), PA_V(256, 0, 0, 2, 1, 4, 2),
-    PA_V(128, 1, 1, 1, 4, 4, 3), PA_V(128, 1, 1, 2, 2, 4, 3), PA_V(128, 1, 1, 4, 2, 4, 2),
-    PA_V(128, 1, 2, 1, 4, 4, 3), PA_V(128, 1, 2, 2, 2, 4, 3), PA_V(128, 1, 2, 4, 2, 4, 2),
+    PA_V(128, 1, 1, 1, 2, 8, 2), PA_V(128, 1, 1, 2, 2, 8, 2), PA_V(128, 1, 1, 4, 2, 4, 2),
+    PA_V(128, 1, 2, 1, 2, 8, 2), PA_V(128, 1, 2, 2, 2, 8, 2), PA_V(128, 1, 2, 4, 2, 4, 2),
     PA_V(256, 1, 1, 1, 2, 4, 3), PA_V(256, 1, 1, 2, 1, 4, 2),
     PA_V(256, 1, 2, 1, 2, 4, 3), PA_V(256, 1, 2, 2, 1, 4, 2),
 };
