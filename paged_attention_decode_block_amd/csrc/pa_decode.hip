@@ -16,8 +16,11 @@
 //
 // Partition pass, one workgroup of NW waves per persistent slot:
 //   * the workgroup walks its segments (token ranges of one (sequence, kv
-//     head) pair); inside a segment wave w takes chunks w, w + NW, ... of
-//     TC = 16 * NB tokens
+//     head) pair); the waves form NW / RS chunk streams of RS waves each;
+//     inside a segment stream s takes chunks s, s + NW / RS, ... of
+//     TC = 16 * NB tokens, and each of its RS waves computes RT 16-row tiles
+//     of the pair's query rows on them (RS > 1 splits many rows over waves
+//     so that each wave's registers allow two waves per SIMD)
 //   * each wave runs an NS-stage software pipeline over its chunk stream:
 //     the K/V rows of chunk i + NS - 1 (16-byte buffer loads straight into
 //     MFMA operand registers) are issued while chunk i is computed, and the
@@ -295,7 +298,7 @@ __device__ __forceinline__ void issue_kv(const DecodeArgs& a, const Entry& e, co
 }
 
 template <int D, bool FP8, int RT>
-__device__ __forceinline__ void load_q(const DecodeArgs& a, const Entry& e, int lane,
+__device__ __forceinline__ void load_q(const DecodeArgs& a, const Entry& e, int lane, int row0,
                                        bf16x8 (&qr)[RT * (D / 32)]) {
   constexpr int KC = D / 32;
   const int c = lane & 15, j = lane >> 4;
@@ -305,7 +308,7 @@ __device__ __forceinline__ void load_q(const DecodeArgs& a, const Entry& e, int 
   for (int rt = 0; rt < RT; ++rt) {
     // rows past R (MFMA padding) reuse the last real row: finite values whose
     // results are never written
-    const int r = min(16 * rt + c, a.rows - 1);
+    const int r = min(row0 + 16 * rt + c, a.rows - 1);
     const int i = r / a.group;
     const int h = e.g * a.group + (r - i * a.group);
     const uint32_t off = static_cast<uint32_t>((i * a.num_q_heads + h) * D) * 2u;
@@ -315,11 +318,13 @@ __device__ __forceinline__ void load_q(const DecodeArgs& a, const Entry& e, int 
   }
 }
 
-template <int D, bool FP8, int SM, int RT, int NB, int NW, int NS>
+template <int D, bool FP8, int SM, int RT, int NB, int NW, int NS, int RS>
 __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(DecodeArgs a) {
   using C = Cfg<D, FP8, RT, NB, NW>;
   constexpr int KC = C::KC, DT = C::DT, TC = C::TC, LPB = C::LPB;
+  constexpr int NST = NW / RS;  // chunk streams
   static_assert(NS == 2 || NS == 3, "2 or 3 K/V register stages");
+  static_assert(NW % RS == 0, "waves split evenly over streams");
   // Prefetch the next segment's Q into registers when they are affordable.
   constexpr bool QPF = RT == 1 || (RT == 2 && NW <= 4);
 
@@ -329,6 +334,8 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int stream = wave / RS, rsub = wave - stream * RS;
+  const int qrow0 = 16 * RT * rsub;  // first query row of this wave
   const int c = lane & 15, j = lane >> 4;
   const int w = blockIdx.x;
 
@@ -337,7 +344,7 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
   cur.s_end = ldu(a.wg_seg_begin, w + 1);
   if (cur.s >= cur.s_end) return;
   cur.live = 1;
-  cursor_load(cur, a, wave);
+  cursor_load(cur, a, stream);
 
   // Softmax scale in the exp2 domain; per-tensor scales are folded in here
   // (K scale into the scores, V scale into the output).
@@ -352,7 +359,7 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
   int row_q[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    const int r = 16 * rt + c;
+    const int r = qrow0 + 16 * rt + c;
     row_q[rt] = r < a.rows ? r / a.group : a.q_len;
   }
 
@@ -366,7 +373,7 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
   constexpr int NE = 2 * NS - 1;
   Entry ev[NE];
 #pragma unroll
-  for (int k = 0; k < NE; ++k) ev[k] = cursor_take<TC, NW>(cur, a, wave);
+  for (int k = 0; k < NE; ++k) ev[k] = cursor_take<TC, NST>(cur, a, stream);
 
   bf16x8 q[RT * KC];
   bf16x8 qn[QPF ? RT * KC : 1];
@@ -383,7 +390,7 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
   // entry NS-1+k and the K/V of entry k
 #pragma unroll
   for (int k = 0; k < NS - 1; ++k) load_pages<NB>(a, ev[k], pg[pslot(k)]);
-  if constexpr (QPF) load_q<D, FP8, RT>(a, ev[0], lane, qn);
+  if constexpr (QPF) load_q<D, FP8, RT>(a, ev[0], lane, qrow0, qn);
 #pragma unroll
   for (int k = 0; k < NS - 1; ++k) {
     load_pages<NB>(a, ev[NS - 1 + k], pg[pslot(NS - 1 + k)]);
@@ -407,7 +414,7 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
 #pragma unroll
         for (int x = 0; x < RT * KC; ++x) q[x] = qn[x];
       } else {
-        load_q<D, FP8, RT>(a, e0, lane, q);
+        load_q<D, FP8, RT>(a, e0, lane, qrow0, q);
       }
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
@@ -419,7 +426,7 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
     }
     load_pages<NB>(a, ev[NE - 1], pg[CUR]);
     if constexpr (QPF) {
-      if (ev[1].live && ev[1].first) load_q<D, FP8, RT>(a, ev[1], lane, qn);
+      if (ev[1].live && ev[1].first) load_q<D, FP8, RT>(a, ev[1], lane, qrow0, qn);
     }
     issue_kv<D, FP8, NB, SM>(a, ev[NS - 1], pg[(CUR + 1) % NS], st[ISS], lane);
 
@@ -572,11 +579,12 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
       }
       __syncthreads();
       const int pair_rows = a.rows;
+      // rows are merged over the NST waves that hold them: waves s RS + rsub
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         float M = neg_inf();
 #pragma unroll
-        for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, st_m[ww][16 * rt + c]);
+        for (int s = 0; s < NST; ++s) M = fmaxf(M, st_m[s * RS + rsub][16 * rt + c]);
         const float Mu = M == neg_inf() ? 0.f : M;
         const float f = __builtin_amdgcn_exp2f(m[rt] - Mu);
         float* ob = reinterpret_cast<float*>(wlds);
@@ -584,20 +592,24 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
         for (int dt = 0; dt < DT; ++dt)
           *reinterpret_cast<f32x4*>(ob + c * C::OROW + 16 * dt + 4 * j) = o[dt][rt] * f;
         __syncthreads();
-        for (int u = threadIdx.x; u < 16 * (D / 8); u += C::THREADS) {
-          const int row = u / (D / 8);
-          const int d0 = (u - row * (D / 8)) * 8;
-          const int r = 16 * rt + row;
+        constexpr int UNITS = 16 * (D / 8);  // (row, 8 dims) units of one wave's tile
+        for (int u = threadIdx.x; u < RS * UNITS; u += C::THREADS) {
+          const int rs = u / UNITS;
+          const int row = (u - rs * UNITS) / (D / 8);
+          const int d0 = (u - rs * UNITS - row * (D / 8)) * 8;
+          const int lr = 16 * rt + row;  // row inside the waves' tiles
+          const int r = 16 * RT * rs + lr;
           if (r < pair_rows) {
             float Mr = neg_inf();
 #pragma unroll
-            for (int ww = 0; ww < NW; ++ww) Mr = fmaxf(Mr, st_m[ww][16 * rt + row]);
+            for (int s = 0; s < NST; ++s) Mr = fmaxf(Mr, st_m[s * RS + rs][lr]);
             const float Mru = Mr == neg_inf() ? 0.f : Mr;
             float L = 0.f;
             f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
 #pragma unroll
-            for (int ww = 0; ww < NW; ++ww) {
-              L += st_l[ww][16 * rt + row] * __builtin_amdgcn_exp2f(st_m[ww][16 * rt + row] - Mru);
+            for (int s = 0; s < NST; ++s) {
+              const int ww = s * RS + rs;
+              L += st_l[ww][lr] * __builtin_amdgcn_exp2f(st_m[ww][lr] - Mru);
               const float* src = reinterpret_cast<const float*>(lds_waves + ww * C::WBYTES) +
                                  row * C::OROW + d0;
               acc0 += *reinterpret_cast<const f32x4*>(src);
@@ -629,7 +641,7 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
 
 #pragma unroll
     for (int k = 0; k < NE - 1; ++k) ev[k] = ev[k + 1];
-    ev[NE - 1] = cursor_take<TC, NW>(cur, a, wave);
+    ev[NE - 1] = cursor_take<TC, NST>(cur, a, stream);
   };
 
   for (;;) {
@@ -739,9 +751,9 @@ __global__ __launch_bounds__(64) void gather_kernel(DecodeArgs a, int row_bytes,
   }
 }
 
-template <int D, bool FP8, int SM, int RT, int NB, int NW, int NS>
+template <int D, bool FP8, int SM, int RT, int NB, int NW, int NS, int RS>
 hipError_t launch_partition_t(const DecodeArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((partition_kernel<D, FP8, SM, RT, NB, NW, NS>), dim3(grid), dim3(NW * 64), 0, s, a);
+  hipLaunchKernelGGL((partition_kernel<D, FP8, SM, RT, NB, NW, NS, RS>), dim3(grid), dim3(NW * 64), 0, s, a);
   return hipGetLastError();
 }
 
@@ -752,15 +764,17 @@ struct VariantEntry {
   LaunchFn fn;
 };
 
-#define PA_V(D, F, SM, RT, NB, NW, NS) \
-  { {D, F, SM, RT, NB, NW, NS}, launch_partition_t<D, F != 0, SM, RT, NB, NW, NS> }
+#define PA_V(D, F, SM, RT, NB, NW, NS, RS) \
+  { {D, F, SM, RT * RS, NB, NW, NS}, launch_partition_t<D, F != 0, SM, RT, NB, NW, NS, RS> }
 const VariantEntry kVariants[] = {
-    PA_V(128, 0, 0, 1, 2, 4, 3), PA_V(128, 0, 0, 2, 2, 4, 3), PA_V(128, 0, 0, 4, 2, 4, 2),
-    PA_V(256, 0, 0, 1, 1, 4, 3), PA_V(256, 0, 0, 2, 1, 4, 2),
-    PA_V(128, 1, 1, 1, 2, 8, 2), PA_V(128, 1, 1, 2, 2, 8, 2), PA_V(128, 1, 1, 4, 2, 4, 2),
-    PA_V(128, 1, 2, 1, 2, 8, 2), PA_V(128, 1, 2, 2, 2, 8, 2), PA_V(128, 1, 2, 4, 2, 4, 2),
-    PA_V(256, 1, 1, 1, 2, 4, 3), PA_V(256, 1, 1, 2, 1, 4, 2),
-    PA_V(256, 1, 2, 1, 2, 4, 3), PA_V(256, 1, 2, 2, 1, 4, 2),
+    // head dim, fp8, scale mode, row tiles per wave, 16-token blocks per
+    // chunk, waves, K/V stages, waves per chunk stream
+    PA_V(128, 0, 0, 1, 2, 4, 3, 1), PA_V(128, 0, 0, 2, 2, 4, 3, 1), PA_V(128, 0, 0, 4, 2, 4, 2, 1),
+    PA_V(256, 0, 0, 1, 1, 4, 3, 1), PA_V(256, 0, 0, 2, 1, 4, 2, 1),
+    PA_V(128, 1, 1, 1, 2, 8, 2, 1), PA_V(128, 1, 1, 2, 2, 8, 2, 1), PA_V(128, 1, 1, 2, 2, 8, 2, 2),
+    PA_V(128, 1, 2, 1, 2, 8, 2, 1), PA_V(128, 1, 2, 2, 2, 8, 2, 1), PA_V(128, 1, 2, 2, 2, 8, 2, 2),
+    PA_V(256, 1, 1, 1, 2, 4, 3, 1), PA_V(256, 1, 1, 2, 1, 4, 2, 1),
+    PA_V(256, 1, 2, 1, 2, 4, 3, 1), PA_V(256, 1, 2, 2, 1, 4, 2, 1),
 };
 #undef PA_V
 
