@@ -661,10 +661,12 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
 // of a split pair with partials (O_s, lse_s): M = max lse_s,
 // w_s = exp(lse_s - M), out = sum w_s O_s / sum w_s ("[Kernel][Perf] Optimize
 // paged-attention metadata decode", ROCm/FlyDSL PR #910, overview: the split
-// reduction kernel). Thread (row, 8 dims) walks the slots four at a time so
-// several partial loads are in flight.
+// reduction kernel). The kernel is latency-bound, so each thread (one row, 8
+// dims) issues the loads of 8 slots at once and folds them in with a running
+// maximum: one round trip for pairs of up to 8 segments.
 constexpr int kReduceThreads = 256;
 constexpr int kReduceRows = 16;
+constexpr int kReduceBatch = 8;
 
 template <int D>
 __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(DecodeArgs a) {
@@ -681,42 +683,39 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(DecodeArgs a) {
     const int d0 = (u % U) * 8;
     if (r >= R) continue;
     const float* lse = a.partial_lse + static_cast<int64_t>(base) * R + r;
-    float M = neg_inf();
-    int s = 0;
-    for (; s + 4 <= n; s += 4) {
-      const float l0 = lse[(s + 0) * R], l1 = lse[(s + 1) * R];
-      const float l2 = lse[(s + 2) * R], l3 = lse[(s + 3) * R];
-      M = fmaxf(M, fmaxf(fmaxf(l0, l1), fmaxf(l2, l3)));
-    }
-    for (; s < n; ++s) M = fmaxf(M, lse[s * R]);
-    const float Mu = M == neg_inf() ? 0.f : M;
     const float* po = a.partial_o + (static_cast<int64_t>(base) * R + r) * D + d0;
     const int64_t so = static_cast<int64_t>(R) * D;  // slot stride in floats
-    float W = 0.f;
+    float M = neg_inf(), W = 0.f;
     f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
-    s = 0;
-    for (; s + 4 <= n; s += 4) {
-      f32x4 x[4][2];
-      float wt[4];
+    for (int s0 = 0; s0 < n; s0 += kReduceBatch) {
+      float lv[kReduceBatch];
+      f32x4 x0[kReduceBatch], x1[kReduceBatch];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        wt[t] = lse[(s + t) * R];
-        x[t][0] = *reinterpret_cast<const f32x4*>(po + (s + t) * so);
-        x[t][1] = *reinterpret_cast<const f32x4*>(po + (s + t) * so + 4);
+      for (int t = 0; t < kReduceBatch; ++t) {
+        lv[t] = neg_inf();
+        x0[t] = x1[t] = f32x4{0, 0, 0, 0};
+        if (s0 + t < n) {
+          lv[t] = lse[(s0 + t) * R];
+          x0[t] = *reinterpret_cast<const f32x4*>(po + (s0 + t) * so);
+          x1[t] = *reinterpret_cast<const f32x4*>(po + (s0 + t) * so + 4);
+        }
       }
+      float mb = M;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const float wgt = __builtin_amdgcn_exp2f((wt[t] - Mu) * kLog2e);
+      for (int t = 0; t < kReduceBatch; ++t) mb = fmaxf(mb, lv[t]);
+      if (mb == neg_inf()) continue;  // every slot so far is empty for this row
+      const float rescale = M == neg_inf() ? 0.f : __builtin_amdgcn_exp2f((M - mb) * kLog2e);
+      W *= rescale;
+      acc0 *= rescale;
+      acc1 *= rescale;
+      M = mb;
+#pragma unroll
+      for (int t = 0; t < kReduceBatch; ++t) {
+        const float wgt = __builtin_amdgcn_exp2f((lv[t] - M) * kLog2e);  // 0 for empty slots
         W += wgt;
-        acc0 += wgt * x[t][0];
-        acc1 += wgt * x[t][1];
+        acc0 += wgt * x0[t];
+        acc1 += wgt * x1[t];
       }
-    }
-    for (; s < n; ++s) {
-      const float wgt = __builtin_amdgcn_exp2f((lse[s * R] - Mu) * kLog2e);
-      W += wgt;
-      acc0 += wgt * *reinterpret_cast<const f32x4*>(po + s * so);
-      acc1 += wgt * *reinterpret_cast<const f32x4*>(po + s * so + 4);
     }
     const float inv = W > 0.f ? 1.f / W : 0.f;
     acc0 *= inv;
