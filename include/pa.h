@@ -140,7 +140,13 @@ typedef struct pa_plan_t {
   uint64_t off_batch_base;     /* int32[batch + 1]: first item of sequence b */
   uint64_t off_partial_lse;    /* float[max_segs][rows]                      */
   uint64_t off_partial_o;      /* float[max_segs][rows][head_dim]            */
-  uint64_t reserved[4];
+  uint64_t off_seg_info;       /* int32[max_segs][8]: each segment as
+                                  (b, g, tok_begin, tok_end, slot, ctx_b,
+                                  pair, 0), read by the decode               */
+  uint64_t off_wg_head;        /* int32[grid][16]: workgroup w's first
+                                  segment, that segment's seg_info record,
+                                  its segment range end, then zeros          */
+  uint64_t reserved[2];
 } pa_plan_t;
 
 #define PA_PLAN_MAGIC 0x50414450u

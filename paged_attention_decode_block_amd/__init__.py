@@ -78,7 +78,8 @@ class pa_plan_t(ctypes.Structure):
         ("off_segs", ctypes.c_uint64), ("off_nseg", ctypes.c_uint64),
         ("off_seg_base", ctypes.c_uint64), ("off_pseg_base", ctypes.c_uint64),
         ("off_batch_base", ctypes.c_uint64), ("off_partial_lse", ctypes.c_uint64),
-        ("off_partial_o", ctypes.c_uint64), ("reserved", ctypes.c_uint64 * 4),
+        ("off_partial_o", ctypes.c_uint64), ("off_seg_info", ctypes.c_uint64),
+        ("off_wg_head", ctypes.c_uint64), ("reserved", ctypes.c_uint64 * 2),
     ]
 
 

@@ -101,7 +101,7 @@ int check_dims(const pa_dims* in, pa_dims* out, int* variant) {
 
 struct Layout {
   uint64_t status, wg_begin, wg_seg_begin, items, segs, nseg, seg_base, pseg_base, batch_base,
-      partial_lse, partial_o, total;
+      partial_lse, partial_o, seg_info, wg_head, total;
   int32_t grid, pairs, rows, max_items, max_segs;
 };
 
@@ -132,6 +132,8 @@ Layout layout(const pa_dims& d, int num_cus) {
   L.batch_base = take(4ull * (d.batch + 1));
   L.partial_lse = take(4ull * L.max_segs * L.rows);
   L.partial_o = take(4ull * L.max_segs * L.rows * d.head_dim);
+  L.seg_info = take(32ull * L.max_segs);
+  L.wg_head = take(64ull * L.grid);
   L.total = off;
   return L;
 }
@@ -194,8 +196,8 @@ pa::DecodeArgs decode_args(const pa_plan_t* plan, const void* q, const void* k_c
   a.v_cache = static_cast<const uint8_t*>(v_cache);
   a.block_table = block_table;
   a.context_lens = context_lens;
-  a.segs = at<const pa::Span>(plan, plan->off_segs);
-  a.wg_seg_begin = at<const int32_t>(plan, plan->off_wg_seg_begin);
+  a.seg_info = at<const int32_t>(plan, plan->off_seg_info);
+  a.wg_head = at<const int32_t>(plan, plan->off_wg_head);
   a.nseg = at<const int32_t>(plan, plan->off_nseg);
   a.seg_base = at<const int32_t>(plan, plan->off_seg_base);
   a.kv_scales = kv_scales;
@@ -311,6 +313,8 @@ int pa_plan(const pa_dims* dims, const int32_t* context_lens, void* workspace,
   p.off_batch_base = L.batch_base;
   p.off_partial_lse = L.partial_lse;
   p.off_partial_o = L.partial_o;
+  p.off_seg_info = L.seg_info;
+  p.off_wg_head = L.wg_head;
 
   pa::PlanArgs a;
   a.context_lens = context_lens;
@@ -323,6 +327,8 @@ int pa_plan(const pa_dims* dims, const int32_t* context_lens, void* workspace,
   a.seg_base = at<int32_t>(&p, p.off_seg_base);
   a.pseg_base = at<int32_t>(&p, p.off_pseg_base);
   a.batch_base = at<int32_t>(&p, p.off_batch_base);
+  a.seg_info = at<int32_t>(&p, p.off_seg_info);
+  a.wg_head = at<int32_t>(&p, p.off_wg_head);
   a.batch = d.batch;
   a.num_kv_heads = d.num_kv_heads;
   a.q_len = d.q_len;

@@ -25,8 +25,8 @@ struct DecodeArgs {
   const uint8_t* v_cache;
   const int32_t* block_table;   // [B, maxp]
   const int32_t* context_lens;  // [B]
-  const Span* segs;
-  const int32_t* wg_seg_begin;
+  const int32_t* seg_info;      // [segs][8] b, g, tok_begin, tok_end, slot, ctx, pair, 0
+  const int32_t* wg_head;       // [grid][16] segment begin, first seg_info record, segment end
   const int32_t* nseg;
   const int32_t* seg_base;
   const float* kv_scales;       // per-token: [2][num_pages][Hkv][ps]

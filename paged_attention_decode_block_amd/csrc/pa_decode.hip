@@ -186,16 +186,22 @@ struct Cursor {
   int32_t live;
 };
 
-__device__ __forceinline__ void cursor_load(Cursor& c, const DecodeArgs& a, int wave) {
-  typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-  const i32x4 sp = ldu(reinterpret_cast<const i32x4*>(a.segs), c.s);  // pair, begin, end, slot
-  c.b = sp.x / a.num_kv_heads;
-  c.g = sp.x - c.b * a.num_kv_heads;
-  c.tb = sp.y;
-  c.te = sp.z;
-  c.slot = sp.w;
-  c.ctx = ldu(a.context_lens, c.b);
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+
+// Segment record (b, g, tok_begin, tok_end, slot, ctx, pair, 0), one scalar
+// load.
+__device__ __forceinline__ void cursor_set(Cursor& c, const i32x8& r, int wave) {
+  c.b = r[0];
+  c.g = r[1];
+  c.tb = r[2];
+  c.te = r[3];
+  c.slot = r[4];
+  c.ctx = r[5];
   c.k = wave;
+}
+
+__device__ __forceinline__ void cursor_load(Cursor& c, const DecodeArgs& a, int wave) {
+  cursor_set(c, ldu(reinterpret_cast<const i32x8*>(a.seg_info), c.s), wave);
 }
 
 template <int TC, int NW>
@@ -339,12 +345,18 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
   const int c = lane & 15, j = lane >> 4;
   const int w = blockIdx.x;
 
+  // the workgroup's header: segment range and first segment, one load
   Cursor cur;
-  cur.s = ldu(a.wg_seg_begin, w);
-  cur.s_end = ldu(a.wg_seg_begin, w + 1);
-  if (cur.s >= cur.s_end) return;
-  cur.live = 1;
-  cursor_load(cur, a, stream);
+  {
+    const i32x8 h0 = ldu(reinterpret_cast<const i32x8*>(a.wg_head), 2 * w);
+    const i32x8 h1 = ldu(reinterpret_cast<const i32x8*>(a.wg_head), 2 * w + 1);
+    cur.s = h0[0];
+    cur.s_end = h1[0];
+    if (cur.s >= cur.s_end) return;
+    cur.live = 1;
+    const i32x8 r = {h0[1], h0[2], h0[3], h0[4], h0[5], h0[6], h0[7], 0};
+    cursor_set(cur, r, stream);
+  }
 
   // Softmax scale in the exp2 domain; per-tensor scales are folded in here
   // (K scale into the scores, V scale into the output).

@@ -159,6 +159,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   const int32_t N = tot.x;
   if (bad) {
     for (int i = gtid; i <= G; i += gstride) { a.wg_begin[i] = 0; a.wg_seg_begin[i] = 0; }
+    for (int i = gtid; i < 16 * G; i += gstride) a.wg_head[i] = 0;
     for (int i = gtid; i < pairs; i += gstride) a.nseg[i] = 0;
     for (int i = gtid; i <= pairs; i += gstride) { a.seg_base[i] = 0; a.pseg_base[i] = 0; }
     for (int i = gtid; i <= B; i += gstride) a.batch_base[i] = 0;
@@ -258,6 +259,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
         Span sg = it;
         sg.tok_end = min((last - A + 1) * P, ctx);
         a.segs[pb + j] = sg;
+        // the decode's record: everything a segment needs in one 32-byte load
+        int4* si = reinterpret_cast<int4*>(a.seg_info + 8 * static_cast<int64_t>(pb + j));
+        si[0] = make_int4(b, g, sg.tok_begin, sg.tok_end);
+        si[1] = make_int4(sg.slot, ctx, p, 0);
       }
       a.items[x] = it;
       if (++k == n && x + 1 < x1) {  // next pair: next kv head, or the next sequence
@@ -277,24 +282,45 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     }
   }
 
-  // 4. per workgroup: its item range and its first segment, the one holding
-  //    item lo(w) (found from the sequence and pair tables)
-  for (int32_t w = gtid; w <= G; w += gstride) {
+  // 4. per workgroup: its item range, its first segment (the one holding item
+  //    lo(w), found from the sequence and pair tables) and its header: the
+  //    first segment's index and decode record, and the segment range end
+  auto first_segment = [&](int32_t w, int4& r0, int4& r1) {
     const int32_t x = sc.wg_lo(w);
-    int32_t first_seg = S;
-    if (w < G) {
-      int lo = 0, hi = B;
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (t.base[mid] <= x) lo = mid; else hi = mid;
-      }
-      const int32_t n = items_of(t.context(lo));
-      const int32_t g = Div(n)(x - t.base[lo]);
-      const int32_t A = t.base[lo] + g * n;
-      first_seg = t.pbase[lo * H + g] + sc.seg_index(x, A);
+    if (w >= G || x >= N) return S;
+    int lo = 0, hi = B;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (t.base[mid] <= x) lo = mid; else hi = mid;
     }
-    a.wg_begin[w] = x;
+    const int32_t ctx = t.context(lo);
+    const int32_t n = items_of(ctx);
+    const int32_t g = Div(n)(x - t.base[lo]);
+    const int32_t A = t.base[lo] + g * n;
+    const int32_t p = lo * H + g;
+    const int32_t j = sc.seg_index(x, A);
+    const int32_t last = min(A + n, sc.wg_lo(sc.owner(x) + 1)) - 1;
+    const int32_t ns = t.nseg[p];
+    r0 = make_int4(lo, g, (x - A) * P, min((last - A + 1) * P, ctx));
+    r1 = make_int4(ns > 1 ? t.sbase[p] + j : -1, ctx, p, 0);
+    return t.pbase[p] + j;
+  };
+  // header of workgroup w: (begin, end, record[8], 0...); the thread of w
+  // writes w's begin and record, and the end of w - 1 (its own begin)
+  for (int32_t w = gtid; w <= G; w += gstride) {
+    int4 r0 = make_int4(0, 0, 0, 0), r1 = make_int4(0, 0, 0, 0);
+    const int32_t first_seg = first_segment(w, r0, r1);
+    a.wg_begin[w] = sc.wg_lo(w);
     a.wg_seg_begin[w] = first_seg;
+    if (w < G) {
+      int4* h = reinterpret_cast<int4*>(a.wg_head + 16 * static_cast<int64_t>(w));
+      h[0] = make_int4(first_seg, r0.x, r0.y, r0.z);
+      h[1] = make_int4(r0.w, r1.x, r1.y, r1.z);
+      h[3] = make_int4(0, 0, 0, 0);
+    }
+    if (w > 0)
+      reinterpret_cast<int4*>(a.wg_head + 16 * static_cast<int64_t>(w - 1))[2] =
+          make_int4(first_seg, 0, 0, 0);
   }
 
   // 5. tables the decode and the tests read, copied out of LDS

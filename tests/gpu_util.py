@@ -99,4 +99,6 @@ def plan_arrays(plan: pa.Plan, batch: int):
         seg_base=plan.region("seg_base", pairs + 1).cpu().tolist(),
         pseg_base=plan.region("pseg_base", pairs + 1).cpu().tolist(),
         batch_base=plan.region("batch_base", batch + 1).cpu().tolist(),
+        seg_info=[tuple(r) for r in plan.region("seg_info", 8 * S).view(-1, 8).cpu().tolist()],
+        wg_head=[tuple(r) for r in plan.region("wg_head", 16 * G).view(-1, 16).cpu().tolist()],
     )

@@ -32,6 +32,22 @@ def _plan_case(ctxs, Hkv, P, q_len, ps, maxp, mult=0, name=""):
     assert got["wg_seg_begin"] == want.wg_seg_begin
     assert got["pseg_base"] == want.pseg_base
     assert got["batch_base"] == want.batch_base
+    # the decode's records: each segment with its sequence, kv head and
+    # context length; each workgroup's segment range and first record
+    want_info = [(p // Hkv, p % Hkv, t0, t1, slot, ctxs[p // Hkv], p, 0)
+                 for p, t0, t1, slot in want.segs]
+    assert got["seg_info"] == want_info
+    G = plan.c.grid
+    for w in range(G):
+        s0, s1 = want.wg_seg_begin[w], want.wg_seg_begin[w + 1]
+        head = got["wg_head"][w]
+        if want.status:
+            assert head == (0,) * 16
+            continue
+        assert (head[0], head[8]) == (s0, s1), f"workgroup {w}"
+        if s0 < s1:
+            assert head[1:8] == want_info[s0][:7], f"workgroup {w}"
+        assert head[9:] == (0,) * 7
     assert pa.pa_plan_status(plan) == want.status
 
 
