@@ -84,7 +84,8 @@ int check_dims(const pa_dims* in, pa_dims* out, int* variant) {
   if (capacity > (int64_t(1) << 30)) return fail(PA_ERR_DIMS, "max_pages_per_seq * page_size too large");
   const int64_t rows = static_cast<int64_t>(d.q_len) * (d.num_q_heads / d.num_kv_heads);
   const int v = pa::pick_variant(d.head_dim, d.kv_dtype == PA_KV_FP8_E4M3FN, d.kv_scale_mode,
-                                 static_cast<int>(rows > 4096 ? 4096 : rows));
+                                 static_cast<int>(rows > 4096 ? 4096 : rows), d.page_size,
+                                 d.partition_size);
   if (rows > 4096 || v < 0)
     return fail(PA_ERR_UNSUPPORTED,
                 "q_len * (num_q_heads / num_kv_heads) = %lld rows per kv head is more than the "

@@ -63,13 +63,14 @@ struct Variant {
   int blocks;
   int waves;
   int stages;
+  int one_page;  // every chunk lies in one page: one block-table entry per chunk
 };
 
 int num_variants();
 const Variant& variant(int i);
 // Returns the index of the instantiation for (head_dim, fp8, scale mode,
 // rows per kv head), or -1.
-int pick_variant(int head_dim, int fp8, int scale_mode, int rows);
+int pick_variant(int head_dim, int fp8, int scale_mode, int rows, int page_size, int partition);
 
 hipError_t launch_partition(int variant, const DecodeArgs& a, int grid, hipStream_t s);
 hipError_t launch_reduce(const DecodeArgs& a, int head_dim, int num_pairs, hipStream_t s);

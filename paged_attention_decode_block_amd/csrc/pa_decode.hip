@@ -233,27 +233,68 @@ __device__ __forceinline__ Entry cursor_take(Cursor& c, const DecodeArgs& a, int
 }
 
 // Block-table entries of an entry's 16-token blocks (one per block: a block
-// never crosses a page). Vector loads of a uniform address, issued a step
-// before the K/V loads that use them; entries past the row read as 0.
-template <int NB>
+// never crosses a page), or a single entry when the whole chunk lies in one
+// page (OPC). Vector loads of a uniform address, issued steps before the K/V
+// loads that use them; entries past the row read as 0.
+template <int NB, bool OPC>
 __device__ __forceinline__ void load_pages(const DecodeArgs& a, const Entry& e, uint32_t (&pg)[NB]) {
   const bool live = e.live && e.data;
   const rsrc_t r = make_rsrc(a.block_table + static_cast<int64_t>(e.b) * a.max_pages,
                              live ? static_cast<uint32_t>(a.max_pages) * 4u : 0u);
 #pragma unroll
-  for (int blk = 0; blk < NB; ++blk) {
+  for (int blk = 0; blk < (OPC ? 1 : NB); ++blk) {
     const uint32_t idx = static_cast<uint32_t>(max(e.tc0 + 16 * blk, 0)) >> a.ps_log2;
     pg[blk] = __builtin_amdgcn_raw_buffer_load_b32(r, idx * 4u, 0, 0);
   }
 }
 
-template <int D, bool FP8, int NB, int SM>
+template <int D, bool FP8, int NB, int SM, bool OPC>
 __device__ __forceinline__ void issue_kv(const DecodeArgs& a, const Entry& e, const uint32_t (&pgv)[NB],
                                          Stage<D, FP8, NB, SM>& st, int lane) {
   constexpr int ROWB = D * (FP8 ? 1 : 2);
   constexpr int LPB = ROWB / 64;
   const int c = lane & 15, j = lane >> 4;
   const int ps_mask = (1 << a.ps_log2) - 1;
+  if constexpr (OPC) {
+    // the chunk's 16 NB rows are consecutive rows of one page: one resource
+    // per array, sized to the rows before the segment end
+    int32_t nl = (e.live && e.data) ? min(max(e.te - e.tc0, 0), 16 * NB) : 0;
+    int32_t page = static_cast<int32_t>(__builtin_amdgcn_readfirstlane(pgv[0]));
+    if (a.debug_bounds && nl > 0 && (page < 0 || page >= a.num_pages)) {
+      nl = 0;
+      atomicOr(a.status + ST_BITS, PA_DEV_BAD_PAGE);
+    }
+    nl = uni(nl);
+    if (nl == 0) page = 0;
+    const uint64_t row0 = uni64(cache_row(page, e.g, e.tc0 & ps_mask, a.num_kv_heads, a.ps_log2));
+    const rsrc_t rk = make_rsrc(a.k_cache + row0 * ROWB, static_cast<uint32_t>(nl * ROWB));
+    const rsrc_t rv = make_rsrc(a.v_cache + row0 * ROWB, static_cast<uint32_t>(nl * ROWB));
+    const uint32_t lane_off = static_cast<uint32_t>(c * ROWB + 16 * j);
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+      for (int i = 0; i < LPB; ++i) st.k[blk][i] = bload16(rk, lane_off + 16 * ROWB * blk + 64 * i);
+    if constexpr (SM == PA_SCALE_PER_TOKEN_HEAD) {
+      const rsrc_t rks = make_rsrc(a.kv_scales + row0, static_cast<uint32_t>(nl * 4));
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk)
+        st.ks[blk] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(rks, 4u * (16 * blk + 4 * j + (c & 3)), 0, 0));
+    }
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+      for (int i = 0; i < LPB; ++i) st.v[blk][i] = bload16(rv, lane_off + 16 * ROWB * blk + 64 * i);
+    if constexpr (SM == PA_SCALE_PER_TOKEN_HEAD) {
+      const uint64_t vplane = static_cast<uint64_t>(a.num_pages) * a.num_kv_heads << a.ps_log2;
+      const rsrc_t rvs = make_rsrc(a.kv_scales + vplane + row0, static_cast<uint32_t>(nl * 4));
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk)
+        st.vs[blk] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(rvs, 4u * (16 * blk + 4 * j + (c & 3)), 0, 0));
+    }
+    return;
+  }
   // Lane (c, j) reads bytes [64 i + 16 j, +16) of row c of each 16-token
   // block; the block's resource covers only its rows before the segment end.
   const uint32_t lane_off = static_cast<uint32_t>(c * ROWB + 16 * j);
@@ -324,7 +365,7 @@ __device__ __forceinline__ void load_q(const DecodeArgs& a, const Entry& e, int 
   }
 }
 
-template <int D, bool FP8, int SM, int RT, int NB, int NW, int NS, int RS>
+template <int D, bool FP8, int SM, int RT, int NB, int NW, int NS, int RS, bool OPC>
 __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(DecodeArgs a) {
   using C = Cfg<D, FP8, RT, NB, NW>;
   constexpr int KC = C::KC, DT = C::DT, TC = C::TC, LPB = C::LPB;
@@ -401,12 +442,12 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
   // first NS-1 entries, Q of entry 0, then for k = 0 .. NS-2 the pages of
   // entry NS-1+k and the K/V of entry k
 #pragma unroll
-  for (int k = 0; k < NS - 1; ++k) load_pages<NB>(a, ev[k], pg[pslot(k)]);
+  for (int k = 0; k < NS - 1; ++k) load_pages<NB, OPC>(a, ev[k], pg[pslot(k)]);
   if constexpr (QPF) load_q<D, FP8, RT>(a, ev[0], lane, qrow0, qn);
 #pragma unroll
   for (int k = 0; k < NS - 1; ++k) {
-    load_pages<NB>(a, ev[NS - 1 + k], pg[pslot(NS - 1 + k)]);
-    issue_kv<D, FP8, NB, SM>(a, ev[k], pg[pslot(k)], st[k], lane);
+    load_pages<NB, OPC>(a, ev[NS - 1 + k], pg[pslot(NS - 1 + k)]);
+    issue_kv<D, FP8, NB, SM, OPC>(a, ev[k], pg[pslot(k)], st[k], lane);
   }
 
   float m[RT], l[RT];
@@ -436,11 +477,11 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
         for (int dt = 0; dt < DT; ++dt) o[dt][rt] = f32x4{0, 0, 0, 0};
       }
     }
-    load_pages<NB>(a, ev[NE - 1], pg[CUR]);
+    load_pages<NB, OPC>(a, ev[NE - 1], pg[CUR]);
     if constexpr (QPF) {
       if (ev[1].live && ev[1].first) load_q<D, FP8, RT>(a, ev[1], lane, qrow0, qn);
     }
-    issue_kv<D, FP8, NB, SM>(a, ev[NS - 1], pg[(CUR + 1) % NS], st[ISS], lane);
+    issue_kv<D, FP8, NB, SM, OPC>(a, ev[NS - 1], pg[(CUR + 1) % NS], st[ISS], lane);
 
     if (e0.data) {
       // ---- S^T = K Q^T: lane holds tokens 16 blk + 4 j + i of row 16 rt + c
@@ -762,9 +803,9 @@ __global__ __launch_bounds__(64) void gather_kernel(DecodeArgs a, int row_bytes,
   }
 }
 
-template <int D, bool FP8, int SM, int RT, int NB, int NW, int NS, int RS>
+template <int D, bool FP8, int SM, int RT, int NB, int NW, int NS, int RS, bool OPC>
 hipError_t launch_partition_t(const DecodeArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((partition_kernel<D, FP8, SM, RT, NB, NW, NS, RS>), dim3(grid), dim3(NW * 64), 0, s, a);
+  hipLaunchKernelGGL((partition_kernel<D, FP8, SM, RT, NB, NW, NS, RS, OPC>), dim3(grid), dim3(NW * 64), 0, s, a);
   return hipGetLastError();
 }
 
@@ -775,17 +816,20 @@ struct VariantEntry {
   LaunchFn fn;
 };
 
-#define PA_V(D, F, SM, RT, NB, NW, NS, RS) \
-  { {D, F, SM, RT * RS, NB, NW, NS}, launch_partition_t<D, F != 0, SM, RT, NB, NW, NS, RS> }
+#define PA_V(D, F, SM, RT, NB, NW, NS, RS, OPC) \
+  { {D, F, SM, RT * RS, NB, NW, NS, OPC}, launch_partition_t<D, F != 0, SM, RT, NB, NW, NS, RS, OPC != 0> }
 const VariantEntry kVariants[] = {
     // head dim, fp8, scale mode, row tiles per wave, 16-token blocks per
-    // chunk, waves, K/V stages, waves per chunk stream
-    PA_V(128, 0, 0, 1, 2, 4, 3, 1), PA_V(128, 0, 0, 2, 2, 4, 3, 1), PA_V(128, 0, 0, 4, 2, 4, 2, 1),
-    PA_V(256, 0, 0, 1, 1, 4, 3, 1), PA_V(256, 0, 0, 2, 1, 4, 2, 1),
-    PA_V(128, 1, 1, 1, 2, 8, 2, 1), PA_V(128, 1, 1, 2, 2, 8, 2, 1), PA_V(128, 1, 1, 2, 2, 8, 2, 2),
-    PA_V(128, 1, 2, 1, 2, 8, 2, 1), PA_V(128, 1, 2, 2, 2, 8, 2, 1), PA_V(128, 1, 2, 2, 2, 8, 2, 2),
-    PA_V(256, 1, 1, 1, 2, 4, 3, 1), PA_V(256, 1, 1, 2, 1, 4, 2, 1),
-    PA_V(256, 1, 2, 1, 2, 4, 3, 1), PA_V(256, 1, 2, 2, 1, 4, 2, 1),
+    // chunk, waves, K/V stages, waves per chunk stream, one page per chunk
+    PA_V(128, 0, 0, 1, 2, 4, 3, 1, 0), PA_V(128, 0, 0, 2, 2, 4, 3, 1, 0), PA_V(128, 0, 0, 4, 2, 4, 2, 1, 0),
+    PA_V(128, 0, 0, 1, 2, 4, 3, 1, 1), PA_V(128, 0, 0, 2, 2, 4, 3, 1, 1), PA_V(128, 0, 0, 4, 2, 4, 2, 1, 1),
+    PA_V(256, 0, 0, 1, 1, 4, 3, 1, 0), PA_V(256, 0, 0, 2, 1, 4, 2, 1, 0),
+    PA_V(128, 1, 1, 1, 2, 8, 2, 1, 0), PA_V(128, 1, 1, 2, 2, 8, 2, 1, 0), PA_V(128, 1, 1, 2, 2, 8, 2, 2, 0),
+    PA_V(128, 1, 1, 1, 2, 8, 2, 1, 1), PA_V(128, 1, 1, 2, 2, 8, 2, 1, 1), PA_V(128, 1, 1, 2, 2, 8, 2, 2, 1),
+    PA_V(128, 1, 2, 1, 2, 8, 2, 1, 0), PA_V(128, 1, 2, 2, 2, 8, 2, 1, 0), PA_V(128, 1, 2, 2, 2, 8, 2, 2, 0),
+    PA_V(128, 1, 2, 1, 2, 8, 2, 1, 1), PA_V(128, 1, 2, 2, 2, 8, 2, 1, 1), PA_V(128, 1, 2, 2, 2, 8, 2, 2, 1),
+    PA_V(256, 1, 1, 1, 2, 4, 3, 1, 0), PA_V(256, 1, 1, 2, 1, 4, 2, 1, 0),
+    PA_V(256, 1, 2, 1, 2, 4, 3, 1, 0), PA_V(256, 1, 2, 2, 1, 4, 2, 1, 0),
 };
 #undef PA_V
 
@@ -795,14 +839,20 @@ int num_variants() { return static_cast<int>(sizeof(kVariants) / sizeof(kVariant
 
 const Variant& variant(int i) { return kVariants[i].v; }
 
-int pick_variant(int head_dim, int fp8, int scale_mode, int rows) {
+int pick_variant(int head_dim, int fp8, int scale_mode, int rows, int page_size, int partition) {
   const int rt = (rows + 15) / 16;
   int best = -1;
   for (int i = 0; i < num_variants(); ++i) {
     const Variant& v = kVariants[i].v;
     if (v.head_dim != head_dim || v.fp8 != fp8 || v.scale_mode != scale_mode || v.row_tiles < rt)
       continue;
-    if (best < 0 || v.row_tiles < kVariants[best].v.row_tiles) best = i;
+    // one page per chunk: chunks start at multiples of the chunk length (a
+    // partition is a whole number of chunks) and a page holds whole chunks
+    const int tc = 16 * v.blocks;
+    if (v.one_page && (page_size < tc || partition % tc != 0)) continue;
+    if (best < 0 || v.row_tiles < kVariants[best].v.row_tiles ||
+        (v.row_tiles == kVariants[best].v.row_tiles && v.one_page > kVariants[best].v.one_page))
+      best = i;
   }
   return best;
 }
