@@ -263,6 +263,18 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
         int4* si = reinterpret_cast<int4*>(a.seg_info + 8 * static_cast<int64_t>(pb + j));
         si[0] = make_int4(b, g, sg.tok_begin, sg.tok_end);
         si[1] = make_int4(sg.slot, ctx, p, 0);
+        if (N >= G && x == lo_w) {
+          // every range is non-empty: this segment opens workgroup w's range
+          int4* h = reinterpret_cast<int4*>(a.wg_head + 16 * static_cast<int64_t>(w));
+          h[0] = make_int4(pb + j, b, g, sg.tok_begin);
+          h[1] = make_int4(sg.tok_end, sg.slot, ctx, p);
+          h[3] = make_int4(0, 0, 0, 0);
+          if (w > 0)
+            reinterpret_cast<int4*>(a.wg_head + 16 * static_cast<int64_t>(w - 1))[2] =
+                make_int4(pb + j, 0, 0, 0);
+          a.wg_begin[w] = x;
+          a.wg_seg_begin[w] = pb + j;
+        }
       }
       a.items[x] = it;
       if (++k == n && x + 1 < x1) {  // next pair: next kv head, or the next sequence
@@ -305,9 +317,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     r1 = make_int4(ns > 1 ? t.sbase[p] + j : -1, ctx, p, 0);
     return t.pbase[p] + j;
   };
-  // header of workgroup w: (begin, end, record[8], 0...); the thread of w
-  // writes w's begin and record, and the end of w - 1 (its own begin)
-  for (int32_t w = gtid; w <= G; w += gstride) {
+  // header of workgroup w: (begin, record[7], end, 0...); the thread of w
+  // writes w's begin and record, and the end of w - 1 (its own begin). When
+  // N >= G the segment that opens each range wrote them already.
+  if (N >= G) {
+    if (gtid == 0) {
+      a.wg_begin[G] = N;
+      a.wg_seg_begin[G] = S;
+      reinterpret_cast<int4*>(a.wg_head + 16 * static_cast<int64_t>(G - 1))[2] = make_int4(S, 0, 0, 0);
+    }
+  } else for (int32_t w = gtid; w <= G; w += gstride) {
     int4 r0 = make_int4(0, 0, 0, 0), r1 = make_int4(0, 0, 0, 0);
     const int32_t first_seg = first_segment(w, r0, r1);
     a.wg_begin[w] = sc.wg_lo(w);
