@@ -162,14 +162,18 @@ int pa_workspace_bytes(const pa_dims* dims, int32_t num_cus, uint64_t* bytes);
 
 /* Build the persistent work list on the current HIP device ([P3] overview:
  * "metadata scheduler"; code excerpt: grid = CUs x multiplier). Launches one
- * workgroup that reads context_lens (device int32[batch]) and writes into
- * `workspace` (device, 256-byte aligned, >= pa_workspace_bytes):
+ * kernel (up to 64 workgroups; one when the batch has more than 4096
+ * sequences or (sequence, kv head) pairs) that reads context_lens (device
+ * int32[batch]) and writes into `workspace` (device, 256-byte aligned,
+ * >= pa_workspace_bytes):
  *   items   for b, then kv head g, then partition k < ceil(ctx_b / P):
  *           (b * Hkv + g, k * P, min((k + 1) * P, ctx_b), slot)
  *   ranges  workgroup w owns items [floor(w N / G), floor((w + 1) N / G))
  *   segments maximal same-pair runs inside one range; a pair with one
  *           segment is finished by its workgroup, the segments of a split
  *           pair get partial slots seg_base[pair] + their index
+ * plus, for the decode, each segment as one 32-byte record (off_seg_info)
+ * and each workgroup's segment range and first record (off_wg_head),
  * and fills *plan. Invalid context lengths set PA_DEV_BAD_CONTEXT in the
  * device status word and give an empty plan. Asynchronous. Errors:
  * PA_ERR_NULL, PA_ERR_DIMS, PA_ERR_UNSUPPORTED, PA_ERR_SCALE_MODE,

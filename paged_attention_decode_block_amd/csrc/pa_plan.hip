@@ -1,4 +1,4 @@
-// Persistent work-list builder (one workgroup).
+// Persistent work-list builder.
 //
 // The metadata scheduler of "[Kernel][Perf] Optimize paged-attention metadata
 // decode" (ROCm/FlyDSL PR #910, "Pull request overview" and the code excerpt:

@@ -149,3 +149,49 @@ def test_split_partials_match_oracle_ranges(name):
         assert (po[slot][~fin] == 0).all()
         checked += 1
     assert checked > 0
+
+
+@pytest.mark.parametrize("name", ["bf16", "fp8_tok_q4"])
+def test_page_size_does_not_change_output_bitwise(name):
+    """The same logical cache in 16-token pages (a chunk spans pages: one
+    block-table entry per 16-token block) and in 64-token pages (a chunk lies
+    in one page: one entry and one descriptor per chunk) gives bit-identical
+    output: the addressing changes, the arithmetic does not."""
+    spec16 = W.scaled(SPECS[name], page_size=16)
+    spec64 = W.scaled(SPECS[name], page_size=64)
+    w16 = W.generate(spec16, 2031)
+    w64 = _same_cache(w16, spec64)
+    say(f"[inv] page size 16 vs 64 {name}")
+    a, _ = run(w16)
+    b, _ = run(w64)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    check(w64, b, f"{name} page 64")
+
+
+def _same_cache(w: W.Workload, spec: W.Spec) -> W.Workload:
+    """w's logical K/V (and scales) re-laid out in pages of spec.page_size, in
+    order: sequence b's pages come one after another."""
+    ps0, ps = w.spec.page_size, spec.page_size
+    B, Hkv, D = w.spec.batch, w.spec.num_kv_heads, w.spec.head_dim
+    ctx = w.context_lens.tolist()
+    pages = [-(-c // ps) for c in ctx]
+    npool = sum(pages)
+    k = torch.zeros((npool, Hkv, ps, D), dtype=w.k_cache.dtype)
+    v = torch.zeros_like(k)
+    per_tok = w.kv_scales is not None and w.kv_scales.dim() == 4
+    sc = torch.zeros((2, npool, Hkv, ps), dtype=torch.float32) if per_tok else w.kv_scales
+    maxp = spec.max_pages_per_seq
+    bt = torch.full((B, maxp), -1, dtype=torch.int32)
+    nxt = 0
+    for b in range(B):
+        for pg in range(pages[b]):
+            bt[b, pg] = nxt + pg
+        for t in range(ctx[b]):
+            src = int(w.block_table[b, t // ps0])
+            dst = nxt + t // ps
+            k[dst, :, t % ps] = w.k_cache[src, :, t % ps0]
+            v[dst, :, t % ps] = w.v_cache[src, :, t % ps0]
+            if per_tok:
+                sc[:, dst, :, t % ps] = w.kv_scales[:, src, :, t % ps0]
+        nxt += pages[b]
+    return W.Workload(spec, w.seed, w.q, k, v, bt, w.context_lens, sc, npool)
