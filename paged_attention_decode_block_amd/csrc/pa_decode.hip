@@ -69,7 +69,10 @@ __device__ __forceinline__ T ldu(const T* p, int64_t i) {
 }
 
 // 8 E4M3FN bytes -> 8 bf16, two per instruction (gfx950 scaled conversion
-// with scale 1). Exact: every finite E4M3FN value is a bf16 value.
+// with scale 1). Exact: every finite E4M3FN value is a bf16 value. (The
+// conversion's scale operand is a power-of-two block scale: only its exponent
+// takes part, so general per-token scales are applied to scores and
+// probabilities instead.)
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
   const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(lo), 1.0f, false);
@@ -91,6 +94,29 @@ __device__ __forceinline__ float quad_bcast(float x, int i) {
     default: r = __builtin_amdgcn_mov_dpp(v, 0xFF, 0xF, 0xF, true); break;
   }
   return __builtin_bit_cast(float, r);
+}
+
+// Reduction over the four 16-lane rows of a wave: every lane gets the result
+// for its column (lane % 16). gfx950 permlane swaps exchange rows in VALU:
+// with both operands a copy of x, the 16-lane swap leaves rows (0, 0, 2, 2)
+// in one result and (1, 1, 3, 3) in the other, the 32-lane swap halves
+// (lo, lo) and (hi, hi).
+__device__ __forceinline__ float pick_max(float a, float b) { return a > b ? a : b; }
+
+template <bool kMax>
+__device__ __forceinline__ float rows_reduce(float x) {
+  // (each element is copied to a scalar before the bit cast: a bit cast of a
+  // vector element in place reads element 0)
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const uint32_t a0u = r16[0], a1u = r16[1];
+  const float a0 = __builtin_bit_cast(float, a0u), a1 = __builtin_bit_cast(float, a1u);
+  x = kMax ? pick_max(a0, a1) : a0 + a1;
+  const uint32_t w = __builtin_bit_cast(uint32_t, x);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  const uint32_t b0u = r32[0], b1u = r32[1];
+  const float b0 = __builtin_bit_cast(float, b0u), b1 = __builtin_bit_cast(float, b1u);
+  return kMax ? pick_max(b0, b1) : b0 + b1;
 }
 
 // LDS transpose read (gfx950 ds_read_b64_tr_b16). Within each 16-lane group,
@@ -484,6 +510,7 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
     issue_kv<D, FP8, NB, SM, OPC>(a, ev[NS - 1], pg[(CUR + 1) % NS], st[ISS], lane);
 
     if (e0.data) {
+      constexpr bool per_tok = SM == PA_SCALE_PER_TOKEN_HEAD;
       // ---- S^T = K Q^T: lane holds tokens 16 blk + 4 j + i of row 16 rt + c
       f32x4 s[NB][RT];
 #pragma unroll
@@ -507,27 +534,32 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
 
       // ---- scale, causal mask, online softmax (exp2 domain). Keys past the
       // segment end were read as zeros; the mask drops them.
+      // Token 16 blk + 4 j + i of the chunk is visible to a row when
+      // 16 blk + i <= lim - tc0 - 4 j: one compare per score (a chunk that no
+      // row masks moves the bound past the chunk).
       const bool full = (e0.tc0 + TC <= e0.te) && (e0.tc0 + TC - 1 <= e0.ctx - a.q_len);
-      constexpr bool per_tok = SM == PA_SCALE_PER_TOKEN_HEAD;
+      // score factor per block: the softmax scale, times the lane quad's
+      // per-token K scales
+      float qk[NB];
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk) qk[blk] = per_tok ? cs.ks[blk] * qk_f : qk_f;
       float pv[NB][RT][4];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         const int lim = min(e0.te - 1, e0.ctx - a.q_len + row_q[rt]);
+        const int vis = full ? TC : lim - e0.tc0 - 4 * j;
         float x[NB][4];
         float cm = neg_inf();
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            float v = s[blk][rt][i] * qk_f;
-            if constexpr (per_tok) v *= quad_bcast(cs.ks[blk], i);
-            if (!full) v = (e0.tc0 + 16 * blk + 4 * j + i <= lim) ? v : neg_inf();
-            x[blk][i] = v;
-            cm = fmaxf(cm, v);
+            const float v = s[blk][rt][i] * (per_tok ? quad_bcast(qk[blk], i) : qk[blk]);
+            x[blk][i] = 16 * blk + i <= vis ? v : neg_inf();
+            cm = fmaxf(cm, x[blk][i]);
           }
         }
-        cm = fmaxf(cm, __shfl_xor(cm, 16));
-        cm = fmaxf(cm, __shfl_xor(cm, 32));
+        cm = rows_reduce<true>(cm);
         // Lazy rescale: keep the running max m while every row's chunk max
         // stays within 2^kSlack of it (then p <= 2^kSlack, exact enough in
         // fp32 and bf16); move it, rescaling l and O, only when some row of
@@ -548,8 +580,7 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
           for (int i = 0; i < 4; ++i) {
             const float p = __builtin_amdgcn_exp2f(x[blk][i] - mu);
             ps += p;
-            if constexpr (per_tok) pv[blk][rt][i] = p * quad_bcast(cs.vs[blk], i);
-            else pv[blk][rt][i] = p;
+            pv[blk][rt][i] = per_tok ? p * quad_bcast(cs.vs[blk], i) : p;
           }
         }
         l[rt] += ps;
@@ -623,8 +654,7 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         float v = l[rt];
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 32);
+        v = rows_reduce<false>(v);
         if (j == 0) {
           st_m[wave][16 * rt + c] = m[rt];
           st_l[wave][16 * rt + c] = v;
