@@ -61,3 +61,34 @@ def e4m3fn_to_f64(codes) -> np.ndarray:
     mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
     mag = np.where((e == 15) & (m == 7), np.nan, mag)
     return np.where(s == 1, -mag, mag)
+
+
+def _e4m3fn_nonneg_values() -> np.ndarray:
+    """Values of the 127 non-negative finite codes 0x00 .. 0x7E, in code order
+    (which is value order)."""
+    return e4m3fn_to_f64(np.arange(0x7F, dtype=np.uint8))
+
+
+def e4m3fn_encode(x) -> np.ndarray:
+    """Finite values with |x| <= 448 -> E4M3FN bytes, round to nearest, ties
+    to even.
+
+    The definition written out: the code whose value is nearest to x; when x
+    lies exactly halfway between two neighbouring codes, the one with mantissa
+    LSB 0 (codes are ordered by value, so that is the even code). The sign bit
+    is set for x < 0 (and for -0.0).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if not np.all(np.isfinite(x)) or np.any(np.abs(x) > 448.0):
+        raise ValueError("e4m3fn_encode takes finite values with |x| <= 448")
+    vals = _e4m3fn_nonneg_values()
+    a = np.abs(x)
+    hi = np.searchsorted(vals, a, side="left")          # first value >= a
+    hi = np.minimum(hi, len(vals) - 1)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - vals[lo]
+    d_hi = vals[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(a == vals[hi], hi, np.where(pick_hi, hi, lo)).astype(np.uint8)
+    neg = np.signbit(x)
+    return np.where(neg, code | 0x80, code).astype(np.uint8)
