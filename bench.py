@@ -20,7 +20,10 @@ The JSON line's `value` is KV-read GB/s of the whole step on the headline
 workload (batched GQA decode); `per_config` carries every workload; `roofline`
 is the partition kernel's algorithmic KV bytes over its mean event duration
 against 8 TB/s; `cpu_baseline` times the CPU oracle on a bounded sample of the
-headline workload, whose outputs also check the GPU's.
+headline workload, whose outputs also check the GPU's. `append` times the
+KV-cache append (the write side, pa_cache_append) at a decode-sized shape (C4's
+32 sequences x 4 new tokens, latency-bound) and at two prefill-sized shapes
+(HBM-bound), with the same flush and events.
 """
 from __future__ import annotations
 
@@ -91,6 +94,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle sample")
+    p.add_argument("--no-append", action="store_true", help="skip the KV-cache append timings")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run one 512 MiB device copy first (a known-size kernel for scaling "
                         "rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -258,6 +262,8 @@ def main():
         del d, ws, out, w
         torch.cuda.empty_cache()
 
+    append = None if args.no_append else append_bench(args, flush)
+
     head = HEADLINE if HEADLINE in results else names[0]
     hr = results[head]
     spec = W.CONFIGS[head]
@@ -307,8 +313,70 @@ def main():
         "cpu_baseline": cpu,
         "parity_sample": parity,
         "per_config": results,
+        "append": append,
     }
     print(json.dumps(line), flush=True)
+
+
+# KV-cache append shapes: (batch, new tokens per sequence, kv heads, head dim,
+# page size, fp8 per-token-head scales or bf16)
+APPEND_SHAPES = {
+    "decode_c4_fp8_per_token": (32, 4, 1, 128, 1024, True),
+    "prefill_fp8_per_token": (32, 4096, 1, 128, 1024, True),
+    "prefill_bf16_c3_heads": (64, 512, 8, 128, 16, False),
+}
+
+
+def append_bench(args, flush):
+    """pa_cache_append timed per launch (median of HIP-event samples after a
+    read flush). Algorithmic bytes: the new K/V rows read (bf16) plus the cache
+    rows written (and the per-token scales)."""
+    import numpy as np
+    import torch
+
+    import paged_attention_decode_block_amd as pa
+
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device="cpu").manual_seed(args.seed)
+    res = {}
+    for name, (B, q_len, hkv, D, ps, fp8) in APPEND_SHAPES.items():
+        maxp = -(-q_len // ps) + 2
+        num_pages = B * maxp
+        ctx = torch.randint(q_len, maxp * ps + 1, (B,), generator=gen, dtype=torch.int32)
+        bt = torch.randperm(num_pages, generator=gen, dtype=torch.int32).view(B, maxp)
+        nk = torch.randn(B, q_len, hkv, D, generator=gen).to(torch.bfloat16).to(dev)
+        nv = torch.randn(B, q_len, hkv, D, generator=gen).to(torch.bfloat16).to(dev)
+        elt = 1 if fp8 else 2
+        kc = torch.zeros(num_pages * hkv * ps * D * elt, dtype=torch.uint8, device=dev)
+        vc = torch.zeros_like(kc)
+        sc = torch.zeros(2 * num_pages * hkv * ps, dtype=torch.float32, device=dev) if fp8 else None
+        dims = pa.make_dims(batch=B, q_len=q_len, num_q_heads=hkv, num_kv_heads=hkv, head_dim=D,
+                            page_size=ps, num_pages=num_pages, max_pages_per_seq=maxp,
+                            kv_dtype=pa.PA_KV_FP8_E4M3FN if fp8 else pa.PA_KV_BF16,
+                            kv_scale_mode=pa.PA_SCALE_PER_TOKEN_HEAD if fp8 else pa.PA_SCALE_NONE)
+        ctx_d, bt_d = ctx.to(dev), bt.to(dev)
+        rows = B * q_len * hkv
+        nbytes = rows * D * 2 * 2 + rows * D * elt * 2 + (rows * 8 if fp8 else 0)
+        us = []
+        for it in range(args.warmup + args.steps):
+            if flush:
+                flush()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            pa.pa_cache_append(dims, nk, nv, bt_d, ctx_d, kc, vc, sc)
+            e1.record()
+            torch.cuda.synchronize()
+            if it >= args.warmup:
+                us.append(e0.elapsed_time(e1) * 1e3)
+        t = statistics.median(us)
+        res[name] = {"rows": rows, "bytes": nbytes, "us": round(t, 3),
+                     "GBps": round(nbytes / t / 1e3, 2),
+                     "frac_of_hbm_peak": round(nbytes / t / 1e3 / HBM_PEAK_GBS, 4)}
+        log(f"append {name}: {rows} rows, {nbytes} bytes in {t:.1f} us -> {nbytes / t / 1e3:.0f} GB/s")
+        del nk, nv, kc, vc, sc
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(keep, seconds):

@@ -223,6 +223,37 @@ int pa_debug_gather(const pa_plan_t* plan, const void* k_cache, const void* v_ca
                     const int32_t* block_table, const int32_t* context_lens, void* k_out,
                     void* v_out, void* stream);
 
+/* KV-cache append, the write side of the cache the decode reads ([P2]
+ * background: K/V live page by page in the paged cache behind the block
+ * table; [P3] overview: the fp8 cache is quantised per token and head or per
+ * tensor). For every sequence b and appended token i < q_len, at position
+ * t = context_lens[b] - q_len + i (context_lens counts the appended tokens,
+ * as in pa_decode), the K and V rows of every kv head g are written to
+ * page block_table[b][t / page_size], slot t % page_size:
+ *   bf16 cache    the rows as they are;
+ *   fp8, per token and head   scale = max_d |x_d| / 448 (1 for an all-zero
+ *                 row) is written to kv_scales[0 or 1][page][g][slot] and the
+ *                 bytes are e4m3fn(clamp(x_d / scale, -448, 448)), rounded to
+ *                 nearest even, every step in float32;
+ *   fp8, per tensor           the same bytes with scale = kv_scales[0] (K) or
+ *                 kv_scales[1] (V), which are read, not written (positive
+ *                 and finite; other scales give unspecified bytes).
+ * new_k, new_v: device bf16 [batch, q_len, num_kv_heads, head_dim], 16-byte
+ * aligned. dims as for pa_plan, except that q_len may be any length (a
+ * prefill appends the whole prompt); num_q_heads, partition_size and
+ * grid_multiplier are validated but not used. k_cache, v_cache, kv_scales,
+ * block_table and context_lens as in pa_decode; kv_scales is NULL exactly
+ * when kv_scale_mode is PA_SCALE_NONE. device_status (optional, device
+ * int32, may be NULL) gets PA_DEV_BAD_CONTEXT for a sequence whose context
+ * length is outside [max(1, q_len), max_pages_per_seq * page_size] and
+ * PA_DEV_BAD_PAGE for a row whose page entry is outside [0, num_pages), OR-ed
+ * in; such rows are not written. No other memory is touched. Asynchronous.
+ * Errors: PA_ERR_NULL, PA_ERR_ALIGN, PA_ERR_DIMS, PA_ERR_UNSUPPORTED,
+ * PA_ERR_SCALE_MODE, PA_ERR_DEVICE, PA_ERR_HIP. */
+int pa_cache_append(const pa_dims* dims, const void* new_k, const void* new_v,
+                    const int32_t* block_table, const int32_t* context_lens, void* k_cache,
+                    void* v_cache, float* kv_scales, int32_t* device_status, void* stream);
+
 /* Static text for a PA_* status code. */
 const char* pa_status_string(int status);
 

@@ -107,6 +107,7 @@ def lib() -> ctypes.CDLL:
             "pa_decode_reduce": (ctypes.c_int, [P(pa_plan_t), i32, i32, vp, vp]),
             "pa_plan_status": (ctypes.c_int, [P(pa_plan_t), P(i32), vp]),
             "pa_debug_gather": (ctypes.c_int, [P(pa_plan_t), vp, vp, vp, vp, vp, vp, vp]),
+            "pa_cache_append": (ctypes.c_int, [P(pa_dims), vp, vp, vp, vp, vp, vp, vp, vp, vp]),
             "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "pa_last_error": (ctypes.c_char_p, []),
         }
@@ -213,6 +214,15 @@ def pa_debug_gather(plan: Plan, k_cache, v_cache, block_table, context_lens, k_o
     _check(lib().pa_debug_gather(ctypes.byref(plan.c), _ptr(k_cache), _ptr(v_cache),
                                  _ptr(block_table), _ptr(context_lens), _ptr(k_out), _ptr(v_out),
                                  _stream(stream)))
+
+
+def pa_cache_append(dims: pa_dims, new_k, new_v, block_table, context_lens, k_cache, v_cache,
+                    kv_scales=None, device_status=None, stream=None):
+    """Write the q_len new tokens' K/V rows of every sequence into the paged
+    cache (include/pa.h, pa_cache_append)."""
+    _check(lib().pa_cache_append(ctypes.byref(dims), _ptr(new_k), _ptr(new_v), _ptr(block_table),
+                                 _ptr(context_lens), _ptr(k_cache), _ptr(v_cache), _ptr(kv_scales),
+                                 _ptr(device_status), _stream(stream)))
 
 
 def pa_status_string(code: int) -> str:

@@ -11,6 +11,7 @@
 #include <mutex>
 #include <string>
 
+#include "pa_cache.h"
 #include "pa_plan.h"
 
 namespace {
@@ -49,8 +50,10 @@ constexpr int kMaxDevices = 64;
 std::mutex g_dev_mu;
 int g_cu_cache[kMaxDevices] = {0};
 
-// Validates dims and applies defaults into *out. Host-only.
-int check_dims(const pa_dims* in, pa_dims* out, int* variant) {
+// Validates dims and applies defaults into *out. Host-only. need_decode:
+// the rows per kv head must fit a decode instantiation (not for the append,
+// which takes any q_len).
+int check_dims(const pa_dims* in, pa_dims* out, int* variant, bool need_decode = true) {
   if (!in) return fail(PA_ERR_NULL, "dims is NULL");
   pa_dims d = *in;
   if (d.partition_size == 0) d.partition_size = kDefaultPartition;
@@ -86,7 +89,7 @@ int check_dims(const pa_dims* in, pa_dims* out, int* variant) {
   const int v = pa::pick_variant(d.head_dim, d.kv_dtype == PA_KV_FP8_E4M3FN, d.kv_scale_mode,
                                  static_cast<int>(rows > 4096 ? 4096 : rows), d.page_size,
                                  d.partition_size);
-  if (rows > 4096 || v < 0)
+  if (need_decode && (rows > 4096 || v < 0))
     return fail(PA_ERR_UNSUPPORTED,
                 "q_len * (num_q_heads / num_kv_heads) = %lld rows per kv head is more than the "
                 "kernels hold for head_dim %d",
@@ -409,6 +412,51 @@ int pa_debug_gather(const pa_plan_t* plan, const void* k_cache, const void* v_ca
                                      static_cast<uint8_t*>(k_out), static_cast<uint8_t*>(v_out),
                                      static_cast<hipStream_t>(stream)),
                    "gather launch") ?: ok();
+}
+
+int pa_cache_append(const pa_dims* dims, const void* new_k, const void* new_v,
+                    const int32_t* block_table, const int32_t* context_lens, void* k_cache,
+                    void* v_cache, float* kv_scales, int32_t* device_status, void* stream) {
+  pa_dims d;
+  int v = -1;
+  if (int rc = check_dims(dims, &d, &v, false)) return rc;
+  if (!new_k || !new_v || !block_table || !context_lens || !k_cache || !v_cache)
+    return fail(PA_ERR_NULL, "new_k, new_v, block_table, context_lens, k_cache and v_cache are required");
+  if (!aligned(new_k, 16) || !aligned(new_v, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
+    return fail(PA_ERR_ALIGN, "new_k, new_v, k_cache and v_cache must be 16-byte aligned");
+  if (!aligned(block_table, 4) || !aligned(context_lens, 4) || !aligned(device_status, 4))
+    return fail(PA_ERR_ALIGN, "block_table, context_lens and device_status must be 4-byte aligned");
+  if ((d.kv_scale_mode == PA_SCALE_NONE) != (kv_scales == nullptr))
+    return fail(PA_ERR_SCALE_MODE, "kv_scales must be NULL exactly when kv_scale_mode is NONE");
+  if (kv_scales && !aligned(kv_scales, 4)) return fail(PA_ERR_ALIGN, "kv_scales must be 4-byte aligned");
+  // element offsets of the new rows stay below 2^31
+  const int64_t rows = static_cast<int64_t>(d.batch) * d.q_len * d.num_kv_heads;
+  if (rows >= (int64_t(1) << 31) / d.head_dim)
+    return fail(PA_ERR_DIMS, "batch * q_len * num_kv_heads = %lld rows is too many for one append",
+                static_cast<long long>(rows));
+  int dev = -1;
+  if (int rc = current_device(&dev)) return rc;
+  int32_t cus = 0;
+  if (int rc = pa_query_device(dev, &cus)) return rc;
+  pa::AppendArgs a;
+  a.new_k = static_cast<const uint16_t*>(new_k);
+  a.new_v = static_cast<const uint16_t*>(new_v);
+  a.block_table = block_table;
+  a.context_lens = context_lens;
+  a.k_cache = static_cast<uint8_t*>(k_cache);
+  a.v_cache = static_cast<uint8_t*>(v_cache);
+  a.kv_scales = kv_scales;
+  a.status = device_status;
+  a.rows = static_cast<int32_t>(rows);
+  a.q_len = d.q_len;
+  a.num_kv_heads = d.num_kv_heads;
+  a.ps_log2 = log2i(d.page_size);
+  a.max_pages = d.max_pages_per_seq;
+  a.num_pages = d.num_pages;
+  a.capacity = d.max_pages_per_seq * d.page_size;
+  return hip_check(pa::launch_append(a, d.head_dim, d.kv_dtype == PA_KV_FP8_E4M3FN, d.kv_scale_mode,
+                                     static_cast<hipStream_t>(stream)),
+                   "append launch") ?: ok();
 }
 
 const char* pa_status_string(int status) {

@@ -130,3 +130,26 @@ def test_status_strings():
         s = pa.pa_status_string(code)
         assert s and s != "unknown status"
     assert pa.pa_status_string(-100) == "unknown status"
+
+
+def _append(d, nk=0x10000, nv=0x18000, bt=0x40000, ctx=0x50000, k=0x20000, v=0x30000,
+            scales=None, status=None):
+    return pa.lib().pa_cache_append(ctypes.byref(d) if d is not None else None, nk, nv, bt, ctx,
+                                    k, v, scales, status, None)
+
+
+def test_cache_append_argument_errors_before_any_device_call():
+    d = _dims()
+    assert _append(None) == pa.PA_ERR_NULL
+    assert _append(d, nk=None) == pa.PA_ERR_NULL
+    assert _append(d, v=None) == pa.PA_ERR_NULL
+    assert _append(_dims(head_dim=64)) == pa.PA_ERR_UNSUPPORTED
+    assert _append(_dims(batch=0)) == pa.PA_ERR_DIMS
+    assert _append(d, nk=0x10008) == pa.PA_ERR_ALIGN
+    assert _append(d, k=0x20004) == pa.PA_ERR_ALIGN
+    assert _append(d, ctx=0x50002) == pa.PA_ERR_ALIGN
+    assert _append(d, status=0x90002) == pa.PA_ERR_ALIGN
+    assert _append(d, scales=0x70000) == pa.PA_ERR_SCALE_MODE
+    f8 = _dims(kv_dtype=pa.PA_KV_FP8_E4M3FN, kv_scale_mode=pa.PA_SCALE_PER_TOKEN_HEAD)
+    assert _append(f8) == pa.PA_ERR_SCALE_MODE
+    assert _append(f8, scales=0x70002) == pa.PA_ERR_ALIGN
