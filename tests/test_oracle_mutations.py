@@ -116,3 +116,54 @@ def test_planted_plan_mistake_is_caught(monkeypatch):
     with pytest.raises(AssertionError):
         for s in range(40):
             TP.test_plan_closed_forms_random(s)
+
+
+def _encode_ties_away(x):
+    # slip: ties rounded away from zero instead of to the even code
+    x = np.asarray(x, dtype=np.float64)
+    vals = codecs._e4m3fn_nonneg_values()
+    a = np.abs(x)
+    hi = np.minimum(np.searchsorted(vals, a, side="left"), len(vals) - 1)
+    lo = np.maximum(hi - 1, 0)
+    code = np.where(vals[hi] - a <= a - vals[lo], hi, lo).astype(np.uint8)
+    return np.where(np.signbit(x), code | 0x80, code).astype(np.uint8)
+
+
+def _encode_truncating(x):
+    # slip: rounds toward zero
+    x = np.asarray(x, dtype=np.float64)
+    vals = codecs._e4m3fn_nonneg_values()
+    a = np.abs(x)
+    code = (np.searchsorted(vals, a, side="right") - 1).astype(np.uint8)
+    return np.where(np.signbit(x), code | 0x80, code).astype(np.uint8)
+
+
+def _cache_pins():
+    from tests import test_oracle_cache as TC
+    TC.test_encode_matches_torch_cast_on_every_bf16_value_and_every_midpoint()
+    TC.test_encode_ties_go_to_the_even_code()
+    TC.test_per_token_append_scale_and_codes()
+    TC.test_per_tensor_append_uses_the_given_scales_and_clamps()
+    TC.test_generator_quantiser_agrees_with_the_oracle_rule()
+
+
+@pytest.mark.parametrize("slip", ["ties away", "truncation", "scale / 240", "multiply by scale"])
+def test_planted_cache_mistake_is_caught(slip, monkeypatch):
+    from oracle import cache
+    if slip == "ties away":
+        monkeypatch.setattr(cache, "e4m3fn_encode", _encode_ties_away)
+        monkeypatch.setattr(codecs, "e4m3fn_encode", _encode_ties_away)
+        monkeypatch.setattr(oracle, "e4m3fn_encode", _encode_ties_away)
+    elif slip == "truncation":
+        monkeypatch.setattr(cache, "e4m3fn_encode", _encode_truncating)
+        monkeypatch.setattr(oracle, "e4m3fn_encode", _encode_truncating)
+    elif slip == "scale / 240":
+        monkeypatch.setattr(cache, "E4M3FN_MAX", np.float32(240.0))   # the FNUZ maximum
+    else:
+        real_quant = cache.quantise_row
+
+        def times_scale(x_f32, scale):
+            return real_quant(x_f32, np.float32(1.0) / (np.float32(scale) ** 2))   # slip: x * s
+        monkeypatch.setattr(cache, "quantise_row", times_scale)
+    with pytest.raises(AssertionError):
+        _cache_pins()
