@@ -84,6 +84,19 @@ def test_row_shapes(q_len, hq, hkv, d):
     check(w, out, spec.name)
 
 
+@pytest.mark.parametrize("mode", [W.SCALE_PER_TOKEN_HEAD, W.SCALE_PER_TENSOR])
+@pytest.mark.parametrize("q_len,hq,hkv", [(8, 16, 16), (1, 16, 1), (2, 16, 1)])
+def test_fp8_head_dim_256(q_len, hq, hkv, mode):
+    # fp8 KV at head_dim 256: rows per kv head 8, 16 and 32 (one and two
+    # 16-row tiles), both scale modes
+    spec = W.Spec(f"fp8_d256_{q_len}x{hq}/{hkv}_{mode}", 3, q_len, hq, hkv, 256, 32, q_len, 900,
+                  kv_dtype=W.KV_FP8, kv_scale_mode=mode, max_ctx=1024)
+    w = W.generate(spec, 2039)
+    say(f"[decode] {spec.name} ctx={w.context_lens.tolist()}")
+    out, _ = run(w)
+    check(w, out, spec.name)
+
+
 @pytest.mark.parametrize("kv", ["bf16", "fp8_tok", "fp8_ten"])
 def test_edge_contexts(kv):
     base = {"bf16": W.scaled(W.C5, batch=6, q_len=4, num_q_heads=8, num_kv_heads=2, head_dim=128),
