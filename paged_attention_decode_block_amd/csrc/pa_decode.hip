@@ -186,12 +186,15 @@ __device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t voff) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
 }
 
-template <int D, bool FP8, int NB, int SM>
+template <int D, bool FP8, int NB, int SM, bool SH = false>
 struct Stage {
   static constexpr int LPB = D * (FP8 ? 1 : 2) / 64;
   static constexpr int NS = SM == PA_SCALE_PER_TOKEN_HEAD ? NB : 1;
+  // rows of K and V; with tiles shared by a stream's two waves, k holds this
+  // wave's half of the chunk (K rows for the first wave, V rows for the
+  // second) and v is unused
   u32x4 k[NB][LPB];
-  u32x4 v[NB][LPB];
+  u32x4 v[SH ? 1 : NB][SH ? 1 : LPB];
   // per-token scales: lane (c, j) holds those of token 4 j + c % 4 of each
   // block; the four tokens of its S^T column come from its lane quad
   float ks[NS];
@@ -230,7 +233,10 @@ __device__ __forceinline__ void cursor_load(Cursor& c, const DecodeArgs& a, int 
   cursor_set(c, ldu(reinterpret_cast<const i32x8*>(a.seg_info), c.s), wave);
 }
 
-template <int TC, int NW>
+// With SH every stream takes the same number of entries per segment,
+// ceil(chunks / NW), the missing chunks as entries without data: the waves
+// then meet one workgroup barrier per step.
+template <int TC, int NW, bool SH = false>
 __device__ __forceinline__ Entry cursor_take(Cursor& c, const DecodeArgs& a, int wave) {
   Entry e;
   e.live = c.live;
@@ -247,7 +253,7 @@ __device__ __forceinline__ Entry cursor_take(Cursor& c, const DecodeArgs& a, int
   e.tc0 = c.tb + TC * c.k;
   e.data = e.tc0 < c.te;
   e.first = c.k == wave;
-  e.last = !e.data || c.tb + TC * (c.k + NW) >= c.te;
+  e.last = SH ? c.tb + TC * (c.k - wave + NW) >= c.te : !e.data || c.tb + TC * (c.k + NW) >= c.te;
   if (!e.last) {
     c.k += NW;
   } else if (++c.s < c.s_end) {
@@ -274,10 +280,12 @@ __device__ __forceinline__ void load_pages(const DecodeArgs& a, const Entry& e, 
   }
 }
 
-template <int D, bool FP8, int NB, int SM, bool OPC>
+template <int D, bool FP8, int NB, int SM, bool OPC, bool SH = false>
 __device__ __forceinline__ void issue_kv(const DecodeArgs& a, const Entry& e, const uint32_t (&pgv)[NB],
-                                         Stage<D, FP8, NB, SM>& st, int lane) {
+                                         Stage<D, FP8, NB, SM, SH>& st, int lane, int rsub = 0) {
   constexpr int ROWB = D * (FP8 ? 1 : 2);
+  // SH: the first wave of the stream loads the K rows, the second the V rows
+  const uint8_t* const kbase = SH && rsub ? a.v_cache : a.k_cache;
   constexpr int LPB = ROWB / 64;
   const int c = lane & 15, j = lane >> 4;
   const int ps_mask = (1 << a.ps_log2) - 1;
@@ -293,7 +301,7 @@ __device__ __forceinline__ void issue_kv(const DecodeArgs& a, const Entry& e, co
     nl = uni(nl);
     if (nl == 0) page = 0;
     const uint64_t row0 = uni64(cache_row(page, e.g, e.tc0 & ps_mask, a.num_kv_heads, a.ps_log2));
-    const rsrc_t rk = make_rsrc(a.k_cache + row0 * ROWB, static_cast<uint32_t>(nl * ROWB));
+    const rsrc_t rk = make_rsrc(kbase + row0 * ROWB, static_cast<uint32_t>(nl * ROWB));
     const rsrc_t rv = make_rsrc(a.v_cache + row0 * ROWB, static_cast<uint32_t>(nl * ROWB));
     const uint32_t lane_off = static_cast<uint32_t>(c * ROWB + 16 * j);
 #pragma unroll
@@ -307,10 +315,12 @@ __device__ __forceinline__ void issue_kv(const DecodeArgs& a, const Entry& e, co
         st.ks[blk] = __builtin_bit_cast(
             float, __builtin_amdgcn_raw_buffer_load_b32(rks, 4u * (16 * blk + 4 * j + (c & 3)), 0, 0));
     }
+    if constexpr (!SH) {
 #pragma unroll
-    for (int blk = 0; blk < NB; ++blk)
+      for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
-      for (int i = 0; i < LPB; ++i) st.v[blk][i] = bload16(rv, lane_off + 16 * ROWB * blk + 64 * i);
+        for (int i = 0; i < LPB; ++i) st.v[blk][i] = bload16(rv, lane_off + 16 * ROWB * blk + 64 * i);
+    }
     if constexpr (SM == PA_SCALE_PER_TOKEN_HEAD) {
       const uint64_t vplane = static_cast<uint64_t>(a.num_pages) * a.num_kv_heads << a.ps_log2;
       const rsrc_t rvs = make_rsrc(a.kv_scales + vplane + row0, static_cast<uint32_t>(nl * 4));
@@ -340,7 +350,7 @@ __device__ __forceinline__ void issue_kv(const DecodeArgs& a, const Entry& e, co
     if (nl == 0) page = 0;
     row0[blk] = uni64(cache_row(page, e.g, t0 & ps_mask, a.num_kv_heads, a.ps_log2));
     nlive[blk] = nl;
-    rk[blk] = make_rsrc(a.k_cache + row0[blk] * ROWB, static_cast<uint32_t>(nl * ROWB));
+    rk[blk] = make_rsrc(kbase + row0[blk] * ROWB, static_cast<uint32_t>(nl * ROWB));
     rv[blk] = make_rsrc(a.v_cache + row0[blk] * ROWB, static_cast<uint32_t>(nl * ROWB));
   }
   // K first, then its scales, then V and its scales: the score math waits for
@@ -356,10 +366,12 @@ __device__ __forceinline__ void issue_kv(const DecodeArgs& a, const Entry& e, co
       st.ks[blk] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rks, 4u * (4 * j + (c & 3)), 0, 0));
     }
   }
+  if constexpr (!SH) {
 #pragma unroll
-  for (int blk = 0; blk < NB; ++blk)
+    for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
-    for (int i = 0; i < LPB; ++i) st.v[blk][i] = bload16(rv[blk], lane_off + 64 * i);
+      for (int i = 0; i < LPB; ++i) st.v[blk][i] = bload16(rv[blk], lane_off + 64 * i);
+  }
   if constexpr (SM == PA_SCALE_PER_TOKEN_HEAD) {
     const uint64_t vplane = static_cast<uint64_t>(a.num_pages) * a.num_kv_heads << a.ps_log2;
 #pragma unroll
@@ -391,17 +403,26 @@ __device__ __forceinline__ void load_q(const DecodeArgs& a, const Entry& e, int 
   }
 }
 
-template <int D, bool FP8, int SM, int RT, int NB, int NW, int NS, int RS, bool OPC>
+template <int D, bool FP8, int SM, int RT, int NB, int NW, int NS, int RS, bool OPC, bool SH>
 __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(DecodeArgs a) {
   using C = Cfg<D, FP8, RT, NB, NW>;
   constexpr int KC = C::KC, DT = C::DT, TC = C::TC, LPB = C::LPB;
   constexpr int NST = NW / RS;  // chunk streams
   static_assert(NS == 2 || NS == 3, "2 or 3 K/V register stages");
   static_assert(NW % RS == 0, "waves split evenly over streams");
+  // SH: the two waves of a stream share the chunk through LDS. Each loads and
+  // widens half of it (the first wave the K rows, the second the V rows)
+  // into a bf16 tile of the stream; after a workgroup barrier both read K and
+  // V from the tiles. The tiles alternate between two buffers by step, and a
+  // segment merge puts the waves' O tiles in the current buffer (its first
+  // barrier follows every read of that buffer).
+  static_assert(!SH || (RS == 2 && FP8), "shared tiles pair the two waves of an fp8 stream");
+  constexpr int SHBUF = 2 * C::VBYTES;  // one buffer: K tile, then V tile
+  static_assert(!SH || 2 * C::OBYTES <= SHBUF, "merge tiles fit one buffer");
   // Prefetch the next segment's Q into registers when they are affordable.
   constexpr bool QPF = RT == 1 || (RT == 2 && NW <= 4);
 
-  __shared__ __attribute__((aligned(16))) uint8_t lds_waves[NW * C::WBYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_waves[SH ? NST * 2 * SHBUF : NW * C::WBYTES];
   __shared__ float st_m[NW][RT * 16];
   __shared__ float st_l[NW][RT * 16];
 
@@ -442,7 +463,10 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
     row_q[rt] = r < a.rows ? r / a.group : a.q_len;
   }
 
-  uint8_t* const wlds = lds_waves + wave * C::WBYTES;
+  uint8_t* const wlds = lds_waves + (SH ? 0 : wave * C::WBYTES);
+  // SH: buffer p of stream s; the step's buffer alternates (par)
+  const auto sh_buf = [&](int s_, int p) { return lds_waves + (s_ * 2 + p) * SHBUF; };
+  int par = 0;
 
   // The wave's chunk stream: ev[0] is computed, ev[1 .. NS-1] have K/V in
   // flight, ev[NS .. 2NS-2] have block-table pages in flight. Pages are
@@ -452,11 +476,11 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
   constexpr int NE = 2 * NS - 1;
   Entry ev[NE];
 #pragma unroll
-  for (int k = 0; k < NE; ++k) ev[k] = cursor_take<TC, NST>(cur, a, stream);
+  for (int k = 0; k < NE; ++k) ev[k] = cursor_take<TC, NST, SH>(cur, a, stream);
 
   bf16x8 q[RT * KC];
   bf16x8 qn[QPF ? RT * KC : 1];
-  Stage<D, FP8, NB, SM> st[NS];
+  Stage<D, FP8, NB, SM, SH> st[NS];
 #pragma unroll
   for (int k = 0; k < NS; ++k) st[k] = {};
   // pages of stream entry m live in pg[(m + 2) % NS] (NS = 3) / pg[m % 2]
@@ -473,7 +497,7 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
 #pragma unroll
   for (int k = 0; k < NS - 1; ++k) {
     load_pages<NB, OPC>(a, ev[NS - 1 + k], pg[pslot(NS - 1 + k)]);
-    issue_kv<D, FP8, NB, SM, OPC>(a, ev[k], pg[pslot(k)], st[k], lane);
+    issue_kv<D, FP8, NB, SM, OPC, SH>(a, ev[k], pg[pslot(k)], st[k], lane, rsub);
   }
 
   float m[RT], l[RT];
@@ -486,7 +510,7 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
   auto step = [&](auto cur_tag) {
     constexpr int CUR = decltype(cur_tag)::value;
     constexpr int ISS = (CUR + NS - 1) % NS;
-    Stage<D, FP8, NB, SM>& cs = st[CUR];
+    Stage<D, FP8, NB, SM, SH>& cs = st[CUR];
     const Entry& e0 = ev[0];
     if (e0.first) {
       if constexpr (QPF) {
@@ -507,7 +531,28 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
     if constexpr (QPF) {
       if (ev[1].live && ev[1].first) load_q<D, FP8, RT>(a, ev[1], lane, qrow0, qn);
     }
-    issue_kv<D, FP8, NB, SM, OPC>(a, ev[NS - 1], pg[(CUR + 1) % NS], st[ISS], lane);
+    issue_kv<D, FP8, NB, SM, OPC, SH>(a, ev[NS - 1], pg[(CUR + 1) % NS], st[ISS], lane, rsub);
+
+    // SH: this wave's half of the chunk, widened, into the stream's tile;
+    // every wave meets the barrier once per step
+    uint8_t* const ktile = SH ? sh_buf(stream, par) : nullptr;
+    uint8_t* const vtile = SH ? sh_buf(stream, par) + C::VBYTES : wlds;
+    if constexpr (SH) {
+      if (e0.data) {
+        uint8_t* const mine = sh_buf(stream, par) + rsub * C::VBYTES;
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) {
+          uint8_t* row = mine + (16 * blk + c) * C::VROW;
+#pragma unroll
+          for (int i = 0; i < LPB; ++i) {
+            const u32x4 wv = cs.k[blk][i];
+            *reinterpret_cast<bf16x8*>(row + 128 * i + 32 * j) = fp8x8_to_bf16(wv.x, wv.y);
+            *reinterpret_cast<bf16x8*>(row + 128 * i + 32 * j + 16) = fp8x8_to_bf16(wv.z, wv.w);
+          }
+        }
+      }
+      __syncthreads();
+    }
 
     if (e0.data) {
       constexpr bool per_tok = SM == PA_SCALE_PER_TOKEN_HEAD;
@@ -520,7 +565,10 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
           bf16x8 kf;
-          if constexpr (FP8) {
+          if constexpr (SH) {
+            kf = *reinterpret_cast<const bf16x8*>(ktile + (16 * blk + c) * C::VROW +
+                                                  2 * qk_dim<FP8>(kc, j));
+          } else if constexpr (FP8) {
             const u32x4 wv = cs.k[blk][kc >> 1];
             kf = (kc & 1) ? fp8x8_to_bf16(wv.z, wv.w) : fp8x8_to_bf16(wv.x, wv.y);
           } else {
@@ -586,19 +634,22 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
         l[rt] += ps;
       }
 
-      // ---- V rows -> wave-private LDS tile (row-major bf16)
+      // ---- V rows -> wave-private LDS tile (row-major bf16); SH: already
+      // in the stream's tile
+      if constexpr (!SH) {
 #pragma unroll
-      for (int blk = 0; blk < NB; ++blk) {
-        uint8_t* vrow = wlds + (16 * blk + c) * C::VROW;
+        for (int blk = 0; blk < NB; ++blk) {
+          uint8_t* vrow = wlds + (16 * blk + c) * C::VROW;
 #pragma unroll
-        for (int i = 0; i < LPB; ++i) {
-          const u32x4 wv = cs.v[blk][i];
-          if constexpr (FP8) {
-            uint8_t* dst = vrow + 128 * i + 32 * j;
-            *reinterpret_cast<bf16x8*>(dst + 0) = fp8x8_to_bf16(wv.x, wv.y);
-            *reinterpret_cast<bf16x8*>(dst + 16) = fp8x8_to_bf16(wv.z, wv.w);
-          } else {
-            *reinterpret_cast<u32x4*>(vrow + 64 * i + 16 * j) = wv;
+          for (int i = 0; i < LPB; ++i) {
+            const u32x4 wv = cs.v[blk][i];
+            if constexpr (FP8) {
+              uint8_t* dst = vrow + 128 * i + 32 * j;
+              *reinterpret_cast<bf16x8*>(dst + 0) = fp8x8_to_bf16(wv.x, wv.y);
+              *reinterpret_cast<bf16x8*>(dst + 16) = fp8x8_to_bf16(wv.z, wv.w);
+            } else {
+              *reinterpret_cast<u32x4*>(vrow + 64 * i + 16 * j) = wv;
+            }
           }
         }
       }
@@ -607,7 +658,7 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
       // order). Lane (c, j) addresses token row 4 j + c / 4 (+16 per block),
       // dims 16 dt + 4 (c % 4): the transpose read hands it tokens
       // 4 j .. 4 j + 3 of dim 16 dt + c.
-      const uint8_t* vt = wlds + (4 * j + (c >> 2)) * C::VROW + 8 * (c & 3);
+      const uint8_t* vt = vtile + (4 * j + (c >> 2)) * C::VROW + 8 * (c & 3);
       if constexpr (NB == 1) {
         bf16x4 bp[RT];
 #pragma unroll
@@ -670,7 +721,7 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
         for (int s = 0; s < NST; ++s) M = fmaxf(M, st_m[s * RS + rsub][16 * rt + c]);
         const float Mu = M == neg_inf() ? 0.f : M;
         const float f = __builtin_amdgcn_exp2f(m[rt] - Mu);
-        float* ob = reinterpret_cast<float*>(wlds);
+        float* ob = reinterpret_cast<float*>(SH ? sh_buf(stream, par) + rsub * C::OBYTES : wlds);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
           *reinterpret_cast<f32x4*>(ob + c * C::OROW + 16 * dt + 4 * j) = o[dt][rt] * f;
@@ -693,8 +744,8 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
             for (int s = 0; s < NST; ++s) {
               const int ww = s * RS + rs;
               L += st_l[ww][lr] * __builtin_amdgcn_exp2f(st_m[ww][lr] - Mru);
-              const float* src = reinterpret_cast<const float*>(lds_waves + ww * C::WBYTES) +
-                                 row * C::OROW + d0;
+              const uint8_t* obw = SH ? sh_buf(s, par) + rs * C::OBYTES : lds_waves + ww * C::WBYTES;
+              const float* src = reinterpret_cast<const float*>(obw) + row * C::OROW + d0;
               acc0 += *reinterpret_cast<const f32x4*>(src);
               acc1 += *reinterpret_cast<const f32x4*>(src + 4);
             }
@@ -724,7 +775,8 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
 
 #pragma unroll
     for (int k = 0; k < NE - 1; ++k) ev[k] = ev[k + 1];
-    ev[NE - 1] = cursor_take<TC, NST>(cur, a, stream);
+    ev[NE - 1] = cursor_take<TC, NST, SH>(cur, a, stream);
+    if constexpr (SH) par ^= 1;
   };
 
   for (;;) {
@@ -833,9 +885,9 @@ __global__ __launch_bounds__(64) void gather_kernel(DecodeArgs a, int row_bytes,
   }
 }
 
-template <int D, bool FP8, int SM, int RT, int NB, int NW, int NS, int RS, bool OPC>
+template <int D, bool FP8, int SM, int RT, int NB, int NW, int NS, int RS, bool OPC, bool SH>
 hipError_t launch_partition_t(const DecodeArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((partition_kernel<D, FP8, SM, RT, NB, NW, NS, RS, OPC>), dim3(grid), dim3(NW * 64), 0, s, a);
+  hipLaunchKernelGGL((partition_kernel<D, FP8, SM, RT, NB, NW, NS, RS, OPC, SH>), dim3(grid), dim3(NW * 64), 0, s, a);
   return hipGetLastError();
 }
 
@@ -847,21 +899,25 @@ struct VariantEntry {
 };
 
 #define PA_V(D, F, SM, RT, NB, NW, NS, RS, OPC) \
-  { {D, F, SM, RT * RS, NB, NW, NS, OPC}, launch_partition_t<D, F != 0, SM, RT, NB, NW, NS, RS, OPC != 0> }
+  { {D, F, SM, RT * RS, NB, NW, NS, OPC}, launch_partition_t<D, F != 0, SM, RT, NB, NW, NS, RS, OPC != 0, false> }
+#define PA_VS(D, F, SM, RT, NB, NW, NS, RS, OPC) \
+  { {D, F, SM, RT * RS, NB, NW, NS, OPC}, launch_partition_t<D, F != 0, SM, RT, NB, NW, NS, RS, OPC != 0, true> }
 const VariantEntry kVariants[] = {
     // head dim, fp8, scale mode, row tiles per wave, 16-token blocks per
-    // chunk, waves, K/V stages, waves per chunk stream, one page per chunk
+    // chunk, waves, K/V stages, waves per chunk stream, one page per chunk;
+    // PA_VS: the stream's two waves share the chunk's K and V tiles in LDS
     PA_V(128, 0, 0, 1, 2, 4, 3, 1, 0), PA_V(128, 0, 0, 2, 2, 4, 3, 1, 0), PA_V(128, 0, 0, 4, 2, 4, 2, 1, 0),
     PA_V(128, 0, 0, 1, 2, 4, 3, 1, 1), PA_V(128, 0, 0, 2, 2, 4, 3, 1, 1), PA_V(128, 0, 0, 4, 2, 4, 2, 1, 1),
     PA_V(256, 0, 0, 1, 1, 4, 3, 1, 0), PA_V(256, 0, 0, 2, 1, 4, 2, 1, 0),
-    PA_V(128, 1, 1, 1, 2, 8, 2, 1, 0), PA_V(128, 1, 1, 2, 2, 8, 2, 1, 0), PA_V(128, 1, 1, 2, 2, 8, 2, 2, 0),
-    PA_V(128, 1, 1, 1, 2, 8, 2, 1, 1), PA_V(128, 1, 1, 2, 2, 8, 2, 1, 1), PA_V(128, 1, 1, 2, 2, 8, 2, 2, 1),
-    PA_V(128, 1, 2, 1, 2, 8, 2, 1, 0), PA_V(128, 1, 2, 2, 2, 8, 2, 1, 0), PA_V(128, 1, 2, 2, 2, 8, 2, 2, 0),
-    PA_V(128, 1, 2, 1, 2, 8, 2, 1, 1), PA_V(128, 1, 2, 2, 2, 8, 2, 1, 1), PA_V(128, 1, 2, 2, 2, 8, 2, 2, 1),
+    PA_V(128, 1, 1, 1, 2, 8, 2, 1, 0), PA_V(128, 1, 1, 2, 2, 8, 2, 1, 0), PA_VS(128, 1, 1, 2, 2, 8, 2, 2, 0),
+    PA_V(128, 1, 1, 1, 2, 8, 2, 1, 1), PA_V(128, 1, 1, 2, 2, 8, 2, 1, 1), PA_VS(128, 1, 1, 2, 2, 8, 2, 2, 1),
+    PA_V(128, 1, 2, 1, 2, 8, 2, 1, 0), PA_V(128, 1, 2, 2, 2, 8, 2, 1, 0), PA_VS(128, 1, 2, 2, 2, 8, 2, 2, 0),
+    PA_V(128, 1, 2, 1, 2, 8, 2, 1, 1), PA_V(128, 1, 2, 2, 2, 8, 2, 1, 1), PA_VS(128, 1, 2, 2, 2, 8, 2, 2, 1),
     PA_V(256, 1, 1, 1, 2, 4, 3, 1, 0), PA_V(256, 1, 1, 2, 1, 4, 2, 1, 0),
     PA_V(256, 1, 2, 1, 2, 4, 3, 1, 0), PA_V(256, 1, 2, 2, 1, 4, 2, 1, 0),
 };
 #undef PA_V
+#undef PA_VS
 
 }  // namespace
 
