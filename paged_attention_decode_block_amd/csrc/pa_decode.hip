@@ -186,15 +186,17 @@ __device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t voff) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
 }
 
-template <int D, bool FP8, int NB, int SM, bool SH = false>
+template <int D, bool FP8, int NB, int SM, int SHR = 0>
 struct Stage {
   static constexpr int LPB = D * (FP8 ? 1 : 2) / 64;
   static constexpr int NS = SM == PA_SCALE_PER_TOKEN_HEAD ? NB : 1;
-  // rows of K and V; with tiles shared by a stream's two waves, k holds this
-  // wave's half of the chunk (K rows for the first wave, V rows for the
-  // second) and v is unused
-  u32x4 k[NB][LPB];
-  u32x4 v[SH ? 1 : NB][SH ? 1 : LPB];
+  // blocks of one array this wave loads when SHR waves share the chunk
+  static constexpr int NBL = SHR ? 2 * NB / SHR : NB;
+  // rows of K and V; with tiles shared by a stream's SHR waves, k holds this
+  // wave's share of the chunk (wave r: blocks (r / 2) NBL .. + NBL - 1 of K
+  // for even r, of V for odd r) and v is unused
+  u32x4 k[NBL][LPB];
+  u32x4 v[SHR ? 1 : NB][SHR ? 1 : LPB];
   // per-token scales: lane (c, j) holds those of token 4 j + c % 4 of each
   // block; the four tokens of its S^T column come from its lane quad
   float ks[NS];
@@ -280,12 +282,16 @@ __device__ __forceinline__ void load_pages(const DecodeArgs& a, const Entry& e, 
   }
 }
 
-template <int D, bool FP8, int NB, int SM, bool OPC, bool SH = false>
+template <int D, bool FP8, int NB, int SM, bool OPC, int SHR = 0>
 __device__ __forceinline__ void issue_kv(const DecodeArgs& a, const Entry& e, const uint32_t (&pgv)[NB],
-                                         Stage<D, FP8, NB, SM, SH>& st, int lane, int rsub = 0) {
+                                         Stage<D, FP8, NB, SM, SHR>& st, int lane, int rsub = 0) {
+  constexpr bool SH = SHR != 0;
   constexpr int ROWB = D * (FP8 ? 1 : 2);
-  // SH: the first wave of the stream loads the K rows, the second the V rows
-  const uint8_t* const kbase = SH && rsub ? a.v_cache : a.k_cache;
+  constexpr int NBL = Stage<D, FP8, NB, SM, SHR>::NBL;
+  // SH: wave r of the stream loads NBL blocks of K (even r) or V (odd r),
+  // starting at block (r / 2) NBL
+  const uint8_t* const kbase = SH && (rsub & 1) ? a.v_cache : a.k_cache;
+  const int blk0 = SH ? (rsub >> 1) * NBL : 0;
   constexpr int LPB = ROWB / 64;
   const int c = lane & 15, j = lane >> 4;
   const int ps_mask = (1 << a.ps_log2) - 1;
@@ -305,9 +311,9 @@ __device__ __forceinline__ void issue_kv(const DecodeArgs& a, const Entry& e, co
     const rsrc_t rv = make_rsrc(a.v_cache + row0 * ROWB, static_cast<uint32_t>(nl * ROWB));
     const uint32_t lane_off = static_cast<uint32_t>(c * ROWB + 16 * j);
 #pragma unroll
-    for (int blk = 0; blk < NB; ++blk)
+    for (int b = 0; b < NBL; ++b)
 #pragma unroll
-      for (int i = 0; i < LPB; ++i) st.k[blk][i] = bload16(rk, lane_off + 16 * ROWB * blk + 64 * i);
+      for (int i = 0; i < LPB; ++i) st.k[b][i] = bload16(rk, lane_off + 16 * ROWB * (blk0 + b) + 64 * i);
     if constexpr (SM == PA_SCALE_PER_TOKEN_HEAD) {
       const rsrc_t rks = make_rsrc(a.kv_scales + row0, static_cast<uint32_t>(nl * 4));
 #pragma unroll
@@ -356,9 +362,9 @@ __device__ __forceinline__ void issue_kv(const DecodeArgs& a, const Entry& e, co
   // K first, then its scales, then V and its scales: the score math waits for
   // K alone while V is still in flight.
 #pragma unroll
-  for (int blk = 0; blk < NB; ++blk)
+  for (int b = 0; b < NBL; ++b)
 #pragma unroll
-    for (int i = 0; i < LPB; ++i) st.k[blk][i] = bload16(rk[blk], lane_off + 64 * i);
+    for (int i = 0; i < LPB; ++i) st.k[b][i] = bload16(rk[SH ? blk0 + b : b], lane_off + 64 * i);
   if constexpr (SM == PA_SCALE_PER_TOKEN_HEAD) {
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk) {
@@ -410,15 +416,18 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
   constexpr int NST = NW / RS;  // chunk streams
   static_assert(NS == 2 || NS == 3, "2 or 3 K/V register stages");
   static_assert(NW % RS == 0, "waves split evenly over streams");
-  // SH: the two waves of a stream share the chunk through LDS. Each loads and
-  // widens half of it (the first wave the K rows, the second the V rows)
-  // into a bf16 tile of the stream; after a workgroup barrier both read K and
-  // V from the tiles. The tiles alternate between two buffers by step, and a
-  // segment merge puts the waves' O tiles in the current buffer (its first
-  // barrier follows every read of that buffer).
-  static_assert(!SH || (RS == 2 && FP8), "shared tiles pair the two waves of an fp8 stream");
+  // SH: the RS waves of a stream share the chunk through LDS. Each loads and
+  // widens its share of it (wave r: 2 NB / RS blocks of K for even r, of V
+  // for odd r) into the stream's bf16 K and V tiles; after a workgroup
+  // barrier every wave reads K and V from the tiles. The tiles alternate
+  // between two buffers by step; a segment merge puts the waves' O tiles in
+  // the stream's two buffers (its first barrier follows every read of them).
+  static_assert(!SH || ((RS == 2 || (RS == 4 && NB % 2 == 0)) && FP8),
+                "shared tiles: 2 or 4 waves per fp8 stream");
+  constexpr int SHR = SH ? RS : 0;
+  constexpr int NBL = Stage<D, FP8, NB, SM, SHR>::NBL;
   constexpr int SHBUF = 2 * C::VBYTES;  // one buffer: K tile, then V tile
-  static_assert(!SH || 2 * C::OBYTES <= SHBUF, "merge tiles fit one buffer");
+  static_assert(!SH || RS * C::OBYTES <= 2 * SHBUF, "merge tiles fit the stream's buffers");
   // Prefetch the next segment's Q into registers when they are affordable.
   constexpr bool QPF = RT == 1 || (RT == 2 && NW <= 4);
 
@@ -480,7 +489,7 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
 
   bf16x8 q[RT * KC];
   bf16x8 qn[QPF ? RT * KC : 1];
-  Stage<D, FP8, NB, SM, SH> st[NS];
+  Stage<D, FP8, NB, SM, SHR> st[NS];
 #pragma unroll
   for (int k = 0; k < NS; ++k) st[k] = {};
   // pages of stream entry m live in pg[(m + 2) % NS] (NS = 3) / pg[m % 2]
@@ -497,7 +506,7 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
 #pragma unroll
   for (int k = 0; k < NS - 1; ++k) {
     load_pages<NB, OPC>(a, ev[NS - 1 + k], pg[pslot(NS - 1 + k)]);
-    issue_kv<D, FP8, NB, SM, OPC, SH>(a, ev[k], pg[pslot(k)], st[k], lane, rsub);
+    issue_kv<D, FP8, NB, SM, OPC, SHR>(a, ev[k], pg[pslot(k)], st[k], lane, rsub);
   }
 
   float m[RT], l[RT];
@@ -510,7 +519,7 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
   auto step = [&](auto cur_tag) {
     constexpr int CUR = decltype(cur_tag)::value;
     constexpr int ISS = (CUR + NS - 1) % NS;
-    Stage<D, FP8, NB, SM, SH>& cs = st[CUR];
+    Stage<D, FP8, NB, SM, SHR>& cs = st[CUR];
     const Entry& e0 = ev[0];
     if (e0.first) {
       if constexpr (QPF) {
@@ -531,21 +540,22 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
     if constexpr (QPF) {
       if (ev[1].live && ev[1].first) load_q<D, FP8, RT>(a, ev[1], lane, qrow0, qn);
     }
-    issue_kv<D, FP8, NB, SM, OPC, SH>(a, ev[NS - 1], pg[(CUR + 1) % NS], st[ISS], lane, rsub);
+    issue_kv<D, FP8, NB, SM, OPC, SHR>(a, ev[NS - 1], pg[(CUR + 1) % NS], st[ISS], lane, rsub);
 
-    // SH: this wave's half of the chunk, widened, into the stream's tile;
+    // SH: this wave's share of the chunk, widened, into the stream's tiles;
     // every wave meets the barrier once per step
     uint8_t* const ktile = SH ? sh_buf(stream, par) : nullptr;
     uint8_t* const vtile = SH ? sh_buf(stream, par) + C::VBYTES : wlds;
     if constexpr (SH) {
       if (e0.data) {
-        uint8_t* const mine = sh_buf(stream, par) + rsub * C::VBYTES;
+        uint8_t* const mine = sh_buf(stream, par) + (rsub & 1) * C::VBYTES;
+        const int blk0 = (rsub >> 1) * NBL;
 #pragma unroll
-        for (int blk = 0; blk < NB; ++blk) {
-          uint8_t* row = mine + (16 * blk + c) * C::VROW;
+        for (int b = 0; b < NBL; ++b) {
+          uint8_t* row = mine + (16 * (blk0 + b) + c) * C::VROW;
 #pragma unroll
           for (int i = 0; i < LPB; ++i) {
-            const u32x4 wv = cs.k[blk][i];
+            const u32x4 wv = cs.k[b][i];
             *reinterpret_cast<bf16x8*>(row + 128 * i + 32 * j) = fp8x8_to_bf16(wv.x, wv.y);
             *reinterpret_cast<bf16x8*>(row + 128 * i + 32 * j + 16) = fp8x8_to_bf16(wv.z, wv.w);
           }
@@ -721,7 +731,7 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
         for (int s = 0; s < NST; ++s) M = fmaxf(M, st_m[s * RS + rsub][16 * rt + c]);
         const float Mu = M == neg_inf() ? 0.f : M;
         const float f = __builtin_amdgcn_exp2f(m[rt] - Mu);
-        float* ob = reinterpret_cast<float*>(SH ? sh_buf(stream, par) + rsub * C::OBYTES : wlds);
+        float* ob = reinterpret_cast<float*>(SH ? sh_buf(stream, 0) + rsub * C::OBYTES : wlds);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
           *reinterpret_cast<f32x4*>(ob + c * C::OROW + 16 * dt + 4 * j) = o[dt][rt] * f;
@@ -744,7 +754,7 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
             for (int s = 0; s < NST; ++s) {
               const int ww = s * RS + rs;
               L += st_l[ww][lr] * __builtin_amdgcn_exp2f(st_m[ww][lr] - Mru);
-              const uint8_t* obw = SH ? sh_buf(s, par) + rs * C::OBYTES : lds_waves + ww * C::WBYTES;
+              const uint8_t* obw = SH ? sh_buf(s, 0) + rs * C::OBYTES : lds_waves + ww * C::WBYTES;
               const float* src = reinterpret_cast<const float*>(obw) + row * C::OROW + d0;
               acc0 += *reinterpret_cast<const f32x4*>(src);
               acc1 += *reinterpret_cast<const f32x4*>(src + 4);
