@@ -23,7 +23,9 @@ against 8 TB/s; `cpu_baseline` times the CPU oracle on a bounded sample of the
 headline workload, whose outputs also check the GPU's. `append` times the
 KV-cache append (the write side, pa_cache_append) at a decode-sized shape (C4's
 32 sequences x 4 new tokens, latency-bound) and at two prefill-sized shapes
-(HBM-bound), with the same flush and events.
+(HBM-bound), with the same flush and events. `decode_loop` times back-to-back
+decode steps (context bump, append, plan, decode) launched eagerly, replayed
+as one graph per step, and unrolled eight to a graph.
 """
 from __future__ import annotations
 
@@ -95,6 +97,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle sample")
     p.add_argument("--no-append", action="store_true", help="skip the KV-cache append timings")
+    p.add_argument("--no-loop", action="store_true",
+                   help="skip the decode-loop timings (eager vs graph-captured steps)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run one 512 MiB device copy first (a known-size kernel for scaling "
                         "rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -263,6 +267,7 @@ def main():
         torch.cuda.empty_cache()
 
     append = None if args.no_append else append_bench(args, flush)
+    loops = None if args.no_loop else decode_loop_bench(args)
 
     head = HEADLINE if HEADLINE in results else names[0]
     hr = results[head]
@@ -314,6 +319,7 @@ def main():
         "parity_sample": parity,
         "per_config": results,
         "append": append,
+        "decode_loop": loops,
     }
     print(json.dumps(line), flush=True)
 
@@ -376,6 +382,111 @@ def append_bench(args, flush):
         log(f"append {name}: {rows} rows, {nbytes} bytes in {t:.1f} us -> {nbytes / t / 1e3:.0f} GB/s")
         del nk, nv, kc, vc, sc
     torch.cuda.empty_cache()
+    return res
+
+
+# Decode loops timed eagerly and as graphs: workloads and steps per graph
+LOOP_WORKLOADS = ("C1_tiny", "C2_single_seq", "C3_batched_gqa")
+LOOP_STEPS = 8
+
+
+def decode_loop_bench(args):
+    """Back-to-back decode steps of a serving loop, each = context lengths +=
+    q_len on the device, pa_cache_append of the new tokens, pa_plan and
+    pa_decode (five launches). Timed three ways over LOOP_STEPS steps between
+    two HIP events: eager launches, one graph replay per step, and all steps
+    unrolled in one graph; reported per step (median over samples). No flush
+    inside the loop: consecutive steps read the same cache, as a serving loop
+    does, so small caches are served from L2 / the Infinity Cache (C3's 1.1 GB
+    is not). The steps' inputs stay in fixed buffers. Before each sample the
+    context lengths are reset, so every sample rewrites the same slots."""
+    import torch
+
+    import paged_attention_decode_block_amd as pa
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    res = {}
+    S = LOOP_STEPS
+    for name in LOOP_WORKLOADS:
+        spec = W.CONFIGS[name]
+        loop = W.decode_loop(spec, args.seed, S)
+        w = loop.start
+        kc, vc = w.k_cache.to(dev), w.v_cache.to(dev)
+        sc = None if w.kv_scales is None else w.kv_scales.to(dev)
+        bt = w.block_table.to(dev)
+        ctx0 = w.context_lens.to(dev)
+        ctx = ctx0.clone()
+        q, nk, nv = loop.q.to(dev), loop.new_k.to(dev), loop.new_v.to(dev)
+        out = torch.empty_like(q)
+        dims = pa.make_dims(batch=spec.batch, q_len=spec.q_len, num_q_heads=spec.num_q_heads,
+                            num_kv_heads=spec.num_kv_heads, head_dim=spec.head_dim,
+                            page_size=spec.page_size, num_pages=w.num_pages,
+                            max_pages_per_seq=spec.max_pages_per_seq,
+                            kv_dtype={W.KV_BF16: pa.PA_KV_BF16,
+                                      W.KV_FP8: pa.PA_KV_FP8_E4M3FN}[spec.kv_dtype],
+                            kv_scale_mode={W.SCALE_NONE: pa.PA_SCALE_NONE,
+                                           W.SCALE_PER_TENSOR: pa.PA_SCALE_PER_TENSOR,
+                                           W.SCALE_PER_TOKEN_HEAD: pa.PA_SCALE_PER_TOKEN_HEAD}[
+                                spec.kv_scale_mode])
+        mode = dims.kv_scale_mode
+        ws = torch.empty(pa.pa_workspace_bytes(dims, pa.pa_query_device(0)), dtype=torch.uint8,
+                         device=dev)
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+        def step(i):
+            ctx.add_(spec.q_len)
+            pa.pa_cache_append(dims, nk[i], nv[i], bt, ctx, kc, vc, sc, status)
+            plan = pa.pa_plan(dims, ctx, workspace=ws)
+            pa.pa_decode(plan, q[i], kc, vc, bt, ctx, spec.q_len, spec.scale, mode, sc, out[i])
+
+        def capture(fn):
+            st = torch.cuda.Stream()
+            st.wait_stream(torch.cuda.current_stream())
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(st):
+                with torch.cuda.graph(g, stream=st):
+                    fn()
+            torch.cuda.current_stream().wait_stream(st)
+            return g
+
+        g_one = capture(lambda: step(0))
+        g_all = capture(lambda: [step(i) for i in range(S)])
+
+        def eager():
+            for i in range(S):
+                step(i)
+
+        def one():
+            for _ in range(S):
+                g_one.replay()
+
+        def unrolled():
+            g_all.replay()
+
+        r = {"steps_per_sample": S, "launches_per_step": 5}
+        for label, body in (("eager", eager), ("graph_per_step", one), ("graph_unrolled", unrolled)):
+            us = []
+            for it in range(3 + max(5, args.steps // 3)):
+                ctx.copy_(ctx0)
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                body()
+                e1.record()
+                torch.cuda.synchronize()
+                if it >= 3:
+                    us.append(e0.elapsed_time(e1) * 1e3 / S)
+            r[label + "_us_per_step"] = round(statistics.median(us), 3)
+        torch.cuda.synchronize()
+        if int(status.item()) != 0:
+            raise RuntimeError(f"decode loop {name}: append status {int(status.item())}")
+        res[name] = r
+        log(f"decode loop {name}: eager {r['eager_us_per_step']:.1f} us/step, graph per step "
+            f"{r['graph_per_step_us_per_step']:.1f}, {S} steps in one graph "
+            f"{r['graph_unrolled_us_per_step']:.1f}")
+        del g_one, g_all, kc, vc, sc, q, nk, nv, out, ws
+        torch.cuda.empty_cache()
     return res
 
 

@@ -95,7 +95,10 @@ enum { PA_FLAG_DEBUG_BOUNDS = 1 };
  * default (256 tokens; one persistent workgroup per CU, [P3] "Summary"). */
 typedef struct pa_dims {
   int32_t batch;
-  int32_t q_len;               /* appended query tokens per sequence, >= 1   */
+  int32_t q_len;               /* appended query tokens per sequence, >= 1;
+                                  rows per kv head q_len * (num_q_heads /
+                                  num_kv_heads) at most 64 (head_dim 128) or
+                                  32 (head_dim 256), else PA_ERR_UNSUPPORTED */
   int32_t num_q_heads;
   int32_t num_kv_heads;        /* divides num_q_heads                        */
   int32_t head_dim;            /* 128 or 256                                 */

@@ -60,3 +60,27 @@ def test_kv_bytes_counts_payload():
     spec = W.scaled(W.C4_Q1_TOK, batch=2, ctx_lo=1000, ctx_hi=1000, max_ctx=2048)
     w = W.generate(spec, 2026)
     assert w.kv_bytes() == 2 * 2000 * 128 + 2 * 2000 * 4
+
+
+def test_decode_loop_poisons_exactly_the_slots_its_steps_fill():
+    spec = W.scaled(W.C4_Q4_TOK, batch=3, ctx_lo=1030, ctx_hi=2060, max_ctx=3072)
+    steps = 3
+    loop = W.decode_loop(spec, 2026, steps, [1030, 2060, 1800])
+    ref = W.generate(spec, 2026, context_lens=[1030, 2060, 1800])
+    start = loop.start.context_lens.tolist()
+    assert start == [1030 - 12, 2060 - 12, 1800 - 12]
+    assert loop.context_lens_at(steps - 1).tolist() == [1030, 2060, 1800]
+    assert loop.q.shape == (steps, 3, 4, 16, 128) and loop.new_k.shape == (steps, 3, 4, 1, 128)
+    assert torch.equal(loop.q[0].view(torch.int16), loop.start.q.view(torch.int16))
+    bt = loop.start.block_table
+    changed = (loop.start.k_cache != ref.k_cache).any(dim=-1)       # [pages, Hkv, ps]
+    want = torch.zeros_like(changed)
+    for b in range(spec.batch):
+        for t in range(start[b], start[b] + steps * spec.q_len):
+            want[int(bt[b, t // spec.page_size]), :, t % spec.page_size] = True
+    assert torch.equal(changed, want)
+    assert (loop.start.k_cache[want] == 0x7F).all()
+    assert torch.isnan(loop.start.kv_scales[:, want]).all()
+    again = W.decode_loop(spec, 2026, steps, [1030, 2060, 1800])
+    for x, y in ((loop.q, again.q), (loop.new_k, again.new_k), (loop.new_v, again.new_v)):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))

@@ -34,6 +34,10 @@ saturate). Unused pages and the slots of the last page past the context
 length are poisoned with NaN (bf16 0x7FC0, e4m3fn 0x7F, NaN scales) so that a
 kernel which reads them as live data is caught; unused block-table entries
 are -1.
+
+Decode loops (``decode_loop``) start the drawn workload ``steps * q_len``
+tokens before its drawn lengths and draw each step's queries and new tokens'
+K/V from streams [seed, 3], [seed, 4] and [seed, 5].
 """
 from __future__ import annotations
 
@@ -301,6 +305,68 @@ def _poison(spec: Spec, k, v, scales, bt, ctx, unused_pages) -> None:
             vview[pg, :, tail:] = fill
             if per_tok:
                 scales[:, pg, :, tail:] = float("nan")
+
+
+@dataclasses.dataclass
+class DecodeLoop:
+    """Inputs of ``steps`` consecutive decode steps of one workload.
+
+    ``start`` is the state before the first step: its ``context_lens`` are the
+    lengths before the step's tokens are appended; its block table already maps
+    every page the steps will write; the slots the steps will fill are poisoned
+    (so a decode that reads one before its append is caught). Step s appends
+    ``new_k[s]`` / ``new_v[s]`` (bf16, [B, q_len, Hkv, D]) at positions
+    [ctx + s q_len, ctx + (s+1) q_len) and decodes ``q[s]`` ([B, q_len, Hq, D])
+    over the grown context. ``start.q`` is ``q[0]``.
+    """
+
+    start: Workload
+    steps: int
+    q: torch.Tensor
+    new_k: torch.Tensor
+    new_v: torch.Tensor
+
+    def context_lens_at(self, step: int) -> torch.Tensor:
+        """Context lengths seen by the decode of ``step`` (0-based)."""
+        return self.start.context_lens + (step + 1) * self.start.spec.q_len
+
+
+def decode_loop(spec: Spec, seed: int, steps: int,
+                final_context_lens: Optional[list] = None) -> DecodeLoop:
+    """Draw a decode loop: the workload of (spec, seed) at its final lengths
+    (drawn, or ``final_context_lens``), started ``steps * q_len`` tokens
+    earlier. Streams [seed, 3], [seed, 4] and [seed, 5] give the steps'
+    queries, new K and new V, N(0, 1) rounded to bf16."""
+    w = generate(spec, seed, context_lens=final_context_lens)
+    B, ql, D, Hkv, ps = spec.batch, spec.q_len, spec.head_dim, spec.num_kv_heads, spec.page_size
+    end = w.context_lens.numpy().astype(np.int64)
+    start = end - steps * ql
+    if int(start.min()) < ql:
+        raise ValueError(f"{spec.name}: a context is shorter than q_len before the first step")
+    nan = _BF16_NAN if spec.kv_dtype == KV_BF16 else _E4M3FN_NAN
+    kview = w.k_cache.view(torch.int16) if spec.kv_dtype == KV_BF16 else w.k_cache
+    vview = w.v_cache.view(torch.int16) if spec.kv_dtype == KV_BF16 else w.v_cache
+    per_tok = w.kv_scales is not None and w.kv_scales.dim() == 4
+    bt = w.block_table.numpy()
+    for b in range(B):
+        for t in range(int(start[b]), int(end[b])):
+            pg, slot = int(bt[b, t // ps]), t % ps
+            kview[pg, :, slot] = nan
+            vview[pg, :, slot] = nan
+            if per_tok:
+                w.kv_scales[:, pg, :, slot] = float("nan")
+
+    def draw(stream: int, heads: int) -> torch.Tensor:
+        x = _rng(seed, stream).standard_normal(steps * B * ql * heads * D, dtype=np.float32)
+        return _to_bf16(x).view(steps, B, ql, heads, D).contiguous()
+
+    q = draw(3, spec.num_q_heads)
+    nk, nv = draw(4, Hkv), draw(5, Hkv)
+    w0 = Workload(spec=spec, seed=seed, q=q[0].contiguous(), k_cache=w.k_cache,
+                  v_cache=w.v_cache, block_table=w.block_table,
+                  context_lens=torch.from_numpy(start.astype(np.int32)), kv_scales=w.kv_scales,
+                  num_pages=w.num_pages)
+    return DecodeLoop(start=w0, steps=steps, q=q, new_k=nk, new_v=nv)
 
 
 def scaled(spec: Spec, **changes) -> Spec:
