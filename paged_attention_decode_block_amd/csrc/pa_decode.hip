@@ -593,8 +593,8 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
       // ---- scale, causal mask, online softmax (exp2 domain). Keys past the
       // segment end were read as zeros; the mask drops them.
       // Token 16 blk + 4 j + i of the chunk is visible to a row when
-      // 16 blk + i <= lim - tc0 - 4 j: one compare per score (a chunk that no
-      // row masks moves the bound past the chunk).
+      // 16 blk + i <= lim - tc0 - 4 j: one compare per score, skipped (a
+      // wave-uniform branch) in chunks that no row masks.
       const bool full = (e0.tc0 + TC <= e0.te) && (e0.tc0 + TC - 1 <= e0.ctx - a.q_len);
       // score factor per block: the softmax scale, times the lane quad's
       // per-token K scales
@@ -604,18 +604,26 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
       float pv[NB][RT][4];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        const int lim = min(e0.te - 1, e0.ctx - a.q_len + row_q[rt]);
-        const int vis = full ? TC : lim - e0.tc0 - 4 * j;
         float x[NB][4];
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            x[blk][i] = s[blk][rt][i] * (per_tok ? quad_bcast(qk[blk], i) : qk[blk]);
+        }
+        if (!full) {
+          const int vis = min(e0.te - 1, e0.ctx - a.q_len + row_q[rt]) - e0.tc0 - 4 * j;
+#pragma unroll
+          for (int blk = 0; blk < NB; ++blk) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[blk][i] = 16 * blk + i <= vis ? x[blk][i] : neg_inf();
+          }
+        }
         float cm = neg_inf();
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float v = s[blk][rt][i] * (per_tok ? quad_bcast(qk[blk], i) : qk[blk]);
-            x[blk][i] = 16 * blk + i <= vis ? v : neg_inf();
-            cm = fmaxf(cm, x[blk][i]);
-          }
+          for (int i = 0; i < 4; ++i) cm = fmaxf(cm, x[blk][i]);
         }
         cm = rows_reduce<true>(cm);
         // Lazy rescale: keep the running max m while every row's chunk max
