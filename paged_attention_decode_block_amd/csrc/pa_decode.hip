@@ -203,12 +203,20 @@ struct Stage {
   float vs[NS];
 };
 
-// One entry of a wave's chunk stream (wave-uniform values).
+// One entry of a wave's chunk stream (wave-uniform values). 2 NS - 1 of them
+// are in flight per wave, all in scalar registers, so they are kept small:
+// the four flags and the kv head share one word, and the context length is
+// kept as ctx - q_len (the last key position the first query row sees).
 struct Entry {
-  int32_t live;           // entry exists
-  int32_t first, last;    // first / last entry of this wave in its segment
-  int32_t data;           // the chunk holds tokens (else: merge only)
-  int32_t b, g, ctx, te, slot, tc0;
+  // bit 0: the entry exists; 1 / 2: first / last entry of this wave in its
+  // segment; 3: the chunk holds tokens (else: merge only); bits 4..: kv head
+  int32_t fg;
+  int32_t b, cq, te, slot, tc0;
+  __device__ __forceinline__ bool live() const { return fg & 1; }
+  __device__ __forceinline__ bool first() const { return fg & 2; }
+  __device__ __forceinline__ bool last() const { return fg & 4; }
+  __device__ __forceinline__ bool data() const { return fg & 8; }
+  __device__ __forceinline__ int32_t g() const { return fg >> 4; }
 };
 
 struct Cursor {
@@ -241,22 +249,19 @@ __device__ __forceinline__ void cursor_load(Cursor& c, const DecodeArgs& a, int 
 template <int TC, int NW, bool SH = false>
 __device__ __forceinline__ Entry cursor_take(Cursor& c, const DecodeArgs& a, int wave) {
   Entry e;
-  e.live = c.live;
   if (!c.live) {
-    e.first = e.last = e.data = 0;
-    e.b = e.g = e.ctx = e.te = e.slot = e.tc0 = 0;
+    e.fg = e.b = e.cq = e.te = e.slot = e.tc0 = 0;
     return e;
   }
   e.b = c.b;
-  e.g = c.g;
-  e.ctx = c.ctx;
+  e.cq = c.ctx - a.q_len;
   e.te = c.te;
   e.slot = c.slot;
   e.tc0 = c.tb + TC * c.k;
-  e.data = e.tc0 < c.te;
-  e.first = c.k == wave;
-  e.last = SH ? c.tb + TC * (c.k - wave + NW) >= c.te : !e.data || c.tb + TC * (c.k + NW) >= c.te;
-  if (!e.last) {
+  const bool data = e.tc0 < c.te;
+  const bool last = SH ? c.tb + TC * (c.k - wave + NW) >= c.te : !data || c.tb + TC * (c.k + NW) >= c.te;
+  e.fg = 1 | (c.k == wave ? 2 : 0) | (last ? 4 : 0) | (data ? 8 : 0) | (c.g << 4);
+  if (!last) {
     c.k += NW;
   } else if (++c.s < c.s_end) {
     cursor_load(c, a, wave);
@@ -272,7 +277,7 @@ __device__ __forceinline__ Entry cursor_take(Cursor& c, const DecodeArgs& a, int
 // loads that use them; entries past the row read as 0.
 template <int NB, bool OPC>
 __device__ __forceinline__ void load_pages(const DecodeArgs& a, const Entry& e, uint32_t (&pg)[NB]) {
-  const bool live = e.live && e.data;
+  const bool live = e.live() && e.data();
   const rsrc_t r = make_rsrc(a.block_table + static_cast<int64_t>(e.b) * a.max_pages,
                              live ? static_cast<uint32_t>(a.max_pages) * 4u : 0u);
 #pragma unroll
@@ -298,7 +303,7 @@ __device__ __forceinline__ void issue_kv(const DecodeArgs& a, const Entry& e, co
   if constexpr (OPC) {
     // the chunk's 16 NB rows are consecutive rows of one page: one resource
     // per array, sized to the rows before the segment end
-    int32_t nl = (e.live && e.data) ? min(max(e.te - e.tc0, 0), 16 * NB) : 0;
+    int32_t nl = (e.live() && e.data()) ? min(max(e.te - e.tc0, 0), 16 * NB) : 0;
     int32_t page = static_cast<int32_t>(__builtin_amdgcn_readfirstlane(pgv[0]));
     if (a.debug_bounds && nl > 0 && (page < 0 || page >= a.num_pages)) {
       nl = 0;
@@ -306,7 +311,7 @@ __device__ __forceinline__ void issue_kv(const DecodeArgs& a, const Entry& e, co
     }
     nl = uni(nl);
     if (nl == 0) page = 0;
-    const uint64_t row0 = uni64(cache_row(page, e.g, e.tc0 & ps_mask, a.num_kv_heads, a.ps_log2));
+    const uint64_t row0 = uni64(cache_row(page, e.g(), e.tc0 & ps_mask, a.num_kv_heads, a.ps_log2));
     const rsrc_t rk = make_rsrc(kbase + row0 * ROWB, static_cast<uint32_t>(nl * ROWB));
     const rsrc_t rv = make_rsrc(a.v_cache + row0 * ROWB, static_cast<uint32_t>(nl * ROWB));
     const uint32_t lane_off = static_cast<uint32_t>(c * ROWB + 16 * j);
@@ -346,7 +351,7 @@ __device__ __forceinline__ void issue_kv(const DecodeArgs& a, const Entry& e, co
 #pragma unroll
   for (int blk = 0; blk < NB; ++blk) {
     const int32_t t0 = e.tc0 + 16 * blk;
-    int32_t nl = (e.live && e.data) ? min(max(e.te - t0, 0), 16) : 0;
+    int32_t nl = (e.live() && e.data()) ? min(max(e.te - t0, 0), 16) : 0;
     int32_t page = static_cast<int32_t>(__builtin_amdgcn_readfirstlane(pgv[blk]));
     if (a.debug_bounds && nl > 0 && (page < 0 || page >= a.num_pages)) {
       nl = 0;
@@ -354,7 +359,7 @@ __device__ __forceinline__ void issue_kv(const DecodeArgs& a, const Entry& e, co
     }
     nl = uni(nl);
     if (nl == 0) page = 0;
-    row0[blk] = uni64(cache_row(page, e.g, t0 & ps_mask, a.num_kv_heads, a.ps_log2));
+    row0[blk] = uni64(cache_row(page, e.g(), t0 & ps_mask, a.num_kv_heads, a.ps_log2));
     nlive[blk] = nl;
     rk[blk] = make_rsrc(kbase + row0[blk] * ROWB, static_cast<uint32_t>(nl * ROWB));
     rv[blk] = make_rsrc(a.v_cache + row0[blk] * ROWB, static_cast<uint32_t>(nl * ROWB));
@@ -401,7 +406,7 @@ __device__ __forceinline__ void load_q(const DecodeArgs& a, const Entry& e, int 
     // results are never written
     const int r = min(row0 + 16 * rt + c, a.rows - 1);
     const int i = r / a.group;
-    const int h = e.g * a.group + (r - i * a.group);
+    const int h = e.g() * a.group + (r - i * a.group);
     const uint32_t off = static_cast<uint32_t>((i * a.num_q_heads + h) * D) * 2u;
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc)
@@ -521,7 +526,7 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
     constexpr int ISS = (CUR + NS - 1) % NS;
     Stage<D, FP8, NB, SM, SHR>& cs = st[CUR];
     const Entry& e0 = ev[0];
-    if (e0.first) {
+    if (e0.first()) {
       if constexpr (QPF) {
 #pragma unroll
         for (int x = 0; x < RT * KC; ++x) q[x] = qn[x];
@@ -538,7 +543,7 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
     }
     load_pages<NB, OPC>(a, ev[NE - 1], pg[CUR]);
     if constexpr (QPF) {
-      if (ev[1].live && ev[1].first) load_q<D, FP8, RT>(a, ev[1], lane, qrow0, qn);
+      if (ev[1].live() && ev[1].first()) load_q<D, FP8, RT>(a, ev[1], lane, qrow0, qn);
     }
     issue_kv<D, FP8, NB, SM, OPC, SHR>(a, ev[NS - 1], pg[(CUR + 1) % NS], st[ISS], lane, rsub);
 
@@ -547,7 +552,7 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
     uint8_t* const ktile = SH ? sh_buf(stream, par) : nullptr;
     uint8_t* const vtile = SH ? sh_buf(stream, par) + C::VBYTES : wlds;
     if constexpr (SH) {
-      if (e0.data) {
+      if (e0.data()) {
         uint8_t* const mine = sh_buf(stream, par) + (rsub & 1) * C::VBYTES;
         const int blk0 = (rsub >> 1) * NBL;
 #pragma unroll
@@ -564,7 +569,7 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
       __syncthreads();
     }
 
-    if (e0.data) {
+    if (e0.data()) {
       constexpr bool per_tok = SM == PA_SCALE_PER_TOKEN_HEAD;
       // ---- S^T = K Q^T: lane holds tokens 16 blk + 4 j + i of row 16 rt + c
       f32x4 s[NB][RT];
@@ -595,7 +600,7 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
       // Token 16 blk + 4 j + i of the chunk is visible to a row when
       // 16 blk + i <= lim - tc0 - 4 j: one compare per score, skipped (a
       // wave-uniform branch) in chunks that no row masks.
-      const bool full = (e0.tc0 + TC <= e0.te) && (e0.tc0 + TC - 1 <= e0.ctx - a.q_len);
+      const bool full = (e0.tc0 + TC <= e0.te) && (e0.tc0 + TC - 1 <= e0.cq);
       // score factor per block: the softmax scale, times the lane quad's
       // per-token K scales
       float qk[NB];
@@ -612,7 +617,7 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
             x[blk][i] = s[blk][rt][i] * (per_tok ? quad_bcast(qk[blk], i) : qk[blk]);
         }
         if (!full) {
-          const int vis = min(e0.te - 1, e0.ctx - a.q_len + row_q[rt]) - e0.tc0 - 4 * j;
+          const int vis = min(e0.te - 1, e0.cq + row_q[rt]) - e0.tc0 - 4 * j;
 #pragma unroll
           for (int blk = 0; blk < NB; ++blk) {
 #pragma unroll
@@ -718,7 +723,7 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
       }
     }
 
-    if (e0.last) {
+    if (e0.last()) {
       // ---- merge the NW waves' (max, sum, O) of this segment
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
@@ -772,7 +777,7 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
             acc1 *= inv;
             if (e0.slot < 0) {
               const int qi = r / a.group;
-              const int h = e0.g * a.group + (r - qi * a.group);
+              const int h = e0.g() * a.group + (r - qi * a.group);
               const f32x8 f8 = {acc0.x, acc0.y, acc0.z, acc0.w, acc1.x, acc1.y, acc1.z, acc1.w};
               const bf16x8 ob8 = __builtin_convertvector(f8, bf16x8);
               *reinterpret_cast<bf16x8*>(a.out + ((static_cast<int64_t>(e0.b) * a.q_len + qi) *
@@ -799,12 +804,12 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
 
   for (;;) {
     step(std::integral_constant<int, 0>{});
-    if (!ev[0].live) break;
+    if (!ev[0].live()) break;
     step(std::integral_constant<int, 1>{});
-    if (!ev[0].live) break;
+    if (!ev[0].live()) break;
     if constexpr (NS == 3) {
       step(std::integral_constant<int, 2>{});
-      if (!ev[0].live) break;
+      if (!ev[0].live()) break;
     }
   }
 }
