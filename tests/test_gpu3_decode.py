@@ -9,9 +9,11 @@ partitions and a ragged tail.
 import pytest
 import torch
 
+import oracle
 import paged_attention_decode_block_amd as pa
 import workloads as W
-from tests.gpu_util import check, run, say
+from tests.gpu_util import MODE_CODE, check, dims_for, run, say, to_f64, tol, upload
+from tests.helpers import assert_close
 
 pytestmark = pytest.mark.gpu
 
@@ -122,3 +124,26 @@ def test_bad_context_reports_and_writes_nothing():
     w.context_lens[1] = 65                          # past capacity
     out, plan = run(w)
     assert pa.pa_plan_status(plan) == pa.PA_DEV_BAD_CONTEXT
+
+
+@pytest.mark.parametrize("scale", [-0.2, 0.0, 1.5])
+@pytest.mark.parametrize("kv", ["bf16", "fp8_tok", "fp8_ten_q4"])
+def test_softmax_scales(kv, scale):
+    # a negative scale (the max tracks the most negative dot product), zero
+    # (uniform weights over the visible keys) and a large one (scores spread
+    # over tens of exp2 units, so the lazy rescale moves the running max often)
+    spec = {"bf16": W.scaled(W.C3, batch=4, ctx_lo=1, ctx_hi=900, max_ctx=1024),
+            "fp8_tok": W.scaled(W.C4_Q1_TOK, batch=3, ctx_lo=1, ctx_hi=2500, max_ctx=3072),
+            "fp8_ten_q4": W.scaled(W.C4_Q4_TEN, batch=3, ctx_lo=4, ctx_hi=2500, max_ctx=3072)}[kv]
+    w = W.generate(spec, 2029)
+    say(f"[decode] scale {scale} {kv} ctx={w.context_lens.tolist()}")
+    d = upload(w)
+    plan = pa.pa_plan(dims_for(w), d.context_lens)
+    out = torch.empty_like(d.q)
+    pa.pa_decode(plan, d.q, d.k_cache, d.v_cache, d.block_table, d.context_lens, spec.q_len, scale,
+                 MODE_CODE[spec.kv_scale_mode], d.kv_scales, out)
+    want, _ = oracle.decode(w.q, w.k_cache, w.v_cache, w.block_table, w.context_lens, spec.q_len,
+                            scale, spec.page_size, spec.kv_dtype, spec.kv_scale_mode, w.kv_scales)
+    err = assert_close(to_f64(out), want, tol(spec), f"scale {scale} {kv}")
+    assert pa.pa_plan_status(plan) == 0
+    say(f"[decode] scale {scale} {kv}: max abs err {err:.3e}")
