@@ -31,6 +31,10 @@
 //     domain with the causal mask of the appended tokens; O^T += V^T P^T on
 //     MFMA, where P^T comes lane-locally from S^T and V^T is read from a
 //     wave-private LDS tile (V rows written row-major, read transposed)
+//   * 64-row fp8 pairs (RS = 2, SH): a stream's two waves share each chunk
+//     through LDS instead: one loads and widens K, the other V, into
+//     double-buffered bf16 tiles of the stream, and the workgroup meets one
+//     barrier per step (every stream takes the same number of entries)
 //   * at a segment's end the NW waves merge their (max, sum, O) through LDS;
 //     an unsplit pair writes bf16 output, a split pair writes its partial O
 //     and log-sum-exp to its slot
