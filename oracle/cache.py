@@ -35,8 +35,10 @@ E4M3FN_MAX = np.float32(448.0)
 
 
 def quantise_row(x_f32: np.ndarray, scale: np.float32) -> np.ndarray:
-    """e4m3fn(clamp(x / scale, +-448)) with the division in float32."""
-    y = (x_f32.astype(np.float32) / np.float32(scale)).astype(np.float32)
+    """e4m3fn(clamp(x / scale, +-448)) with the division in float32 (a quotient
+    past the float32 range is infinite, and the clamp takes it to +-448)."""
+    with np.errstate(over="ignore"):
+        y = (x_f32.astype(np.float32) / np.float32(scale)).astype(np.float32)
     y = np.clip(y, -E4M3FN_MAX, E4M3FN_MAX)
     return e4m3fn_encode(y)
 

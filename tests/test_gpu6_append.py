@@ -228,3 +228,70 @@ def test_quotients_near_code_boundaries_encode_like_the_oracle():
     wk, wv, ws, _ = cache.append(nk, nv, bt, ctx, q_len, ps, kc, vc, True, True, sc)
     assert st == 0 and np.array_equal(gk, wk) and np.array_equal(gv, wv)
     assert np.array_equal(gs.view(np.uint32), ws.view(np.uint32))
+
+
+def _rows_case(nk_rows, nv_rows, per_token, sc=None):
+    """Rows [n, D] of bf16 bits appended one per sequence (q_len 1, one kv
+    head, page 16): GPU bytes and scales vs the oracle, bit for bit."""
+    n, D = nk_rows.shape
+    q_len, ps = 1, 16
+    nk = nk_rows.reshape(n, q_len, 1, D)
+    nv = nv_rows.reshape(n, q_len, 1, D)
+    ctx = np.full(n, 1, dtype=np.int32)
+    bt = np.arange(n, dtype=np.int32).reshape(n, 1)
+    kc = np.zeros((n, 1, ps, D), dtype=np.uint8)
+    vc = np.zeros_like(kc)
+    mode = pa.PA_SCALE_PER_TOKEN_HEAD if per_token else pa.PA_SCALE_PER_TENSOR
+    if per_token:
+        sc = np.zeros((2, n, 1, ps), dtype=np.float32)
+    dims = _dims(n, q_len, 1, D, ps, n, 1, True, mode)
+    gk, gv, gs, st = _gpu_append(dims, nk, nv, bt, ctx, kc, vc, sc)
+    wk, wv, ws, _ = cache.append(nk, nv, bt, ctx, q_len, ps, kc, vc, True, per_token, sc)
+    assert st == 0
+    bad = np.argwhere(gk != wk)
+    assert np.array_equal(gk, wk), f"K bytes differ at {bad[:5].tolist()}"
+    assert np.array_equal(gv, wv)
+    if per_token:
+        assert np.array_equal(gs.view(np.uint32), ws.view(np.uint32))
+
+
+def test_tiny_rows_and_tiny_scales_encode_like_the_oracle():
+    """Rows whose largest magnitude is tiny (per-token scales down to
+    subnormal float32, where 1 / scale overflows) and tiny per-tensor scales:
+    the quotient x / scale is still an ordinary number, and zeros keep their
+    sign."""
+    r = np.random.default_rng(21)
+    D = 128
+    mags = np.array([2.0 ** -133, 2.0 ** -126, 1e-38, 1e-37, 3e-36, 1e-30, 2.0 ** -61, 2.0 ** -59,
+                     1e-12, 1.0])
+    rows = []
+    for m in mags:
+        x = r.uniform(-1, 1, size=D) * m
+        x[0] = m                                    # the row maximum
+        x[1], x[2] = 0.0, -0.0
+        rows.append(x)
+    bits = _bf16_bits(np.array(rows))
+    bits[:, 2] = 0x8000                             # an explicit -0
+    say("[append] tiny per-token rows")
+    _rows_case(bits, bits[::-1].copy(), per_token=True)
+    for scale in (2.0 ** -149, 1e-40, 2.0 ** -70, 1e-30):
+        say(f"[append] per-tensor scale {scale:g}")
+        _rows_case(bits, bits[::-1].copy(), per_token=False,
+                   sc=np.array([scale, scale * 0.75], dtype=np.float32))
+
+
+def test_every_row_maximum_gives_the_oracle_scale_and_codes():
+    """Per-token rows whose maximum magnitude is each positive finite bf16
+    value in turn: the row scale max / 448 and every code match the oracle
+    bit for bit (the other elements are the maximum times random fractions,
+    rounded to bf16, with signs)."""
+    r = np.random.default_rng(5)
+    D = 128
+    m_bits = np.arange(1, 0x7F80, dtype=np.uint32)          # +bf16 subnormals .. max finite
+    m = (m_bits << np.uint32(16)).view(np.float32).astype(np.float64)
+    x = r.uniform(-1, 1, size=(len(m), D)) * m[:, None]
+    bits = _bf16_bits(x)
+    bits[:, 0] = m_bits.astype(np.uint16)
+    # bf16 rounding of the fractions may not exceed the maximum (|frac| < 1)
+    say(f"[append] {len(m)} rows, every positive finite bf16 maximum")
+    _rows_case(bits, np.roll(bits, 7, axis=0), per_token=True)
