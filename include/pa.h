@@ -203,7 +203,9 @@ int pa_decode(const pa_plan_t* plan, const void* q, const void* k_cache, const v
 /* The two launches of pa_decode, separately: the partition pass (writes the
  * output of unsplit pairs and the partials of split ones) and the reduce
  * (merges the partials). pa_decode == pa_decode_partition then
- * pa_decode_reduce on the same stream; same arguments and errors. */
+ * pa_decode_reduce on the same stream; same arguments and errors. When
+ * partition_size >= max_pages_per_seq * page_size no pair can be split, and
+ * pa_decode_reduce validates its arguments and launches nothing. */
 int pa_decode_partition(const pa_plan_t* plan, const void* q, const void* k_cache,
                         const void* v_cache, const int32_t* block_table,
                         const int32_t* context_lens, int32_t q_len, float scale,

@@ -366,6 +366,10 @@ int pa_decode_reduce(const pa_plan_t* plan, int32_t q_len, int32_t kv_scale_mode
   if (q_len != plan->dims.q_len || kv_scale_mode != plan->dims.kv_scale_mode)
     return fail(PA_ERR_PLAN_MISMATCH, "q_len / kv_scale_mode differ from the plan's");
   if (int rc = check_plan(plan)) return rc;
+  // A context never longer than one partition (partition_size >= the block
+  // table's capacity) makes every pair a single item, hence a single
+  // segment, written out by the partition pass: nothing is left to merge.
+  if (plan->max_items <= plan->num_pairs) return ok();
   pa::DecodeArgs a = decode_args(plan, out, out, out, nullptr, nullptr, 1.0f, nullptr, out);
   return hip_check(pa::launch_reduce(a, plan->dims.head_dim, plan->num_pairs,
                                      static_cast<hipStream_t>(stream)),
