@@ -6,13 +6,15 @@ seeded workloads (unused pages and dead slots poisoned with NaN), at sizes
 the float64 oracle finishes in seconds but that still span several pages,
 partitions and a ragged tail.
 """
+import numpy as np
 import pytest
 import torch
 
 import oracle
 import paged_attention_decode_block_amd as pa
 import workloads as W
-from tests.gpu_util import MODE_CODE, check, dims_for, run, say, to_f64, tol, upload
+from oracle import cache
+from tests.gpu_util import DEV, MODE_CODE, check, dims_for, run, say, to_f64, tol, upload
 from tests.helpers import assert_close
 
 pytestmark = pytest.mark.gpu
@@ -147,3 +149,61 @@ def test_softmax_scales(kv, scale):
     err = assert_close(to_f64(out), want, tol(spec), f"scale {scale} {kv}")
     assert pa.pa_plan_status(plan) == 0
     say(f"[decode] scale {scale} {kv}: max abs err {err:.3e}")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8_tok"])
+def test_pages_beyond_4_gib(kv):
+    """A pool larger than 4 GiB per cache with the workload's pages placed
+    past the first 4 GiB: byte offsets of K, V and per-token scales exceed
+    32 bits. The output equals the oracle's on the compact pool (the result
+    does not depend on where pages sit), and an append through the same
+    table writes the oracle's bytes at those pages."""
+    spec = {"bf16": W.scaled(W.C3, batch=3, ctx_lo=100, ctx_hi=700, max_ctx=1024),
+            "fp8_tok": W.scaled(W.C4_Q4_TOK, batch=2, ctx_lo=900, ctx_hi=2500, max_ctx=3072)}[kv]
+    w = W.generate(spec, 2026)
+    page_bytes = w.k_cache[0].numel() * w.k_cache.element_size()
+    base = (1 << 32) // page_bytes + 17                  # first page past 4 GiB
+    big = base + w.num_pages
+    say(f"[decode] {kv}: {big} pages of {page_bytes} B ({big * page_bytes / 2**30:.1f} GiB per cache)")
+    k_big = torch.empty((big,) + tuple(w.k_cache.shape[1:]), dtype=w.k_cache.dtype, device=DEV)
+    v_big = torch.empty_like(k_big)
+    k_big[base:] = w.k_cache.to(DEV)
+    v_big[base:] = w.v_cache.to(DEV)
+    sc_big = None
+    if w.kv_scales is not None:
+        sc_big = torch.empty((2, big) + tuple(w.kv_scales.shape[2:]), dtype=torch.float32, device=DEV)
+        sc_big[:, base:] = w.kv_scales.to(DEV)
+    bt = torch.where(w.block_table >= 0, w.block_table + base, w.block_table).to(DEV)
+    ctx = w.context_lens.to(DEV)
+    dims = pa.make_dims(batch=spec.batch, q_len=spec.q_len, num_q_heads=spec.num_q_heads,
+                        num_kv_heads=spec.num_kv_heads, head_dim=spec.head_dim,
+                        page_size=spec.page_size, num_pages=big,
+                        max_pages_per_seq=spec.max_pages_per_seq,
+                        kv_dtype=dims_for(w).kv_dtype, kv_scale_mode=dims_for(w).kv_scale_mode)
+    plan = pa.pa_plan(dims, ctx)
+    q = w.q.to(DEV)
+    out = torch.empty_like(q)
+    pa.pa_decode(plan, q, k_big, v_big, bt, ctx, spec.q_len, spec.scale,
+                 MODE_CODE[spec.kv_scale_mode], sc_big, out)
+    assert pa.pa_plan_status(plan) == 0
+    check(w, out, f"beyond 4 GiB {kv}")
+    # the append writes its rows through the same table
+    r = np.random.default_rng(4)
+    nk = torch.from_numpy(r.standard_normal((spec.batch, spec.q_len, spec.num_kv_heads,
+                                             spec.head_dim), dtype=np.float32)).to(torch.bfloat16)
+    nv = torch.from_numpy(r.standard_normal(nk.shape, dtype=np.float32)).to(torch.bfloat16)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    pa.pa_cache_append(dims, nk.to(DEV), nv.to(DEV), bt, ctx, k_big, v_big, sc_big, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    fp8 = spec.kv_dtype == W.KV_FP8
+    bf16_bits = lambda t: t.view(torch.int16).numpy().view(np.uint16)
+    bits = (lambda t: t.numpy()) if fp8 else bf16_bits
+    wk, wv, ws, wst = cache.append(bf16_bits(nk), bf16_bits(nv), w.block_table.numpy(), w.context_lens.numpy(),
+                                   spec.q_len, spec.page_size, bits(w.k_cache), bits(w.v_cache), fp8,
+                                   spec.kv_scale_mode == W.SCALE_PER_TOKEN_HEAD,
+                                   None if w.kv_scales is None else w.kv_scales.numpy())
+    assert wst == 0
+    assert np.array_equal(bits(k_big[base:].cpu()), wk) and np.array_equal(bits(v_big[base:].cpu()), wv)
+    if ws is not None:
+        assert np.array_equal(sc_big[:, base:].cpu().numpy().view(np.uint32), ws.view(np.uint32))
