@@ -186,8 +186,12 @@ __device__ __forceinline__ uint64_t uni64(uint64_t v) {
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
+// 16-byte buffer load. STREAM sets the non-temporal cache policy (each K/V
+// byte is read once): measured 1-4% faster for bf16 caches and 7-8% slower
+// for fp8 ones, so only bf16 K/V loads use it.
+template <bool STREAM = false>
 __device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t voff) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, STREAM ? 2 : 0));
 }
 
 template <int D, bool FP8, int NB, int SM, int SHR = 0>
@@ -322,7 +326,7 @@ __device__ __forceinline__ void issue_kv(const DecodeArgs& a, const Entry& e, co
 #pragma unroll
     for (int b = 0; b < NBL; ++b)
 #pragma unroll
-      for (int i = 0; i < LPB; ++i) st.k[b][i] = bload16(rk, lane_off + 16 * ROWB * (blk0 + b) + 64 * i);
+      for (int i = 0; i < LPB; ++i) st.k[b][i] = bload16<!FP8>(rk, lane_off + 16 * ROWB * (blk0 + b) + 64 * i);
     if constexpr (SM == PA_SCALE_PER_TOKEN_HEAD) {
       const rsrc_t rks = make_rsrc(a.kv_scales + row0, static_cast<uint32_t>(nl * 4));
 #pragma unroll
@@ -334,7 +338,7 @@ __device__ __forceinline__ void issue_kv(const DecodeArgs& a, const Entry& e, co
 #pragma unroll
       for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
-        for (int i = 0; i < LPB; ++i) st.v[blk][i] = bload16(rv, lane_off + 16 * ROWB * blk + 64 * i);
+        for (int i = 0; i < LPB; ++i) st.v[blk][i] = bload16<!FP8>(rv, lane_off + 16 * ROWB * blk + 64 * i);
     }
     if constexpr (SM == PA_SCALE_PER_TOKEN_HEAD) {
       const uint64_t vplane = static_cast<uint64_t>(a.num_pages) * a.num_kv_heads << a.ps_log2;
@@ -373,7 +377,7 @@ __device__ __forceinline__ void issue_kv(const DecodeArgs& a, const Entry& e, co
 #pragma unroll
   for (int b = 0; b < NBL; ++b)
 #pragma unroll
-    for (int i = 0; i < LPB; ++i) st.k[b][i] = bload16(rk[SH ? blk0 + b : b], lane_off + 64 * i);
+    for (int i = 0; i < LPB; ++i) st.k[b][i] = bload16<!FP8>(rk[SH ? blk0 + b : b], lane_off + 64 * i);
   if constexpr (SM == PA_SCALE_PER_TOKEN_HEAD) {
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk) {
@@ -385,7 +389,7 @@ __device__ __forceinline__ void issue_kv(const DecodeArgs& a, const Entry& e, co
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
-      for (int i = 0; i < LPB; ++i) st.v[blk][i] = bload16(rv[blk], lane_off + 64 * i);
+      for (int i = 0; i < LPB; ++i) st.v[blk][i] = bload16<!FP8>(rv[blk], lane_off + 64 * i);
   }
   if constexpr (SM == PA_SCALE_PER_TOKEN_HEAD) {
     const uint64_t vplane = static_cast<uint64_t>(a.num_pages) * a.num_kv_heads << a.ps_log2;
