@@ -95,10 +95,14 @@ enum { PA_FLAG_DEBUG_BOUNDS = 1 };
  * default (256 tokens; one persistent workgroup per CU, [P3] "Summary"). */
 typedef struct pa_dims {
   int32_t batch;
-  int32_t q_len;               /* appended query tokens per sequence, >= 1;
-                                  rows per kv head q_len * (num_q_heads /
-                                  num_kv_heads) at most 64 (head_dim 128) or
-                                  32 (head_dim 256), else PA_ERR_UNSUPPORTED */
+  int32_t q_len;               /* appended query tokens per sequence, >= 1.
+                                  When the rows per kv head, q_len *
+                                  (num_q_heads / num_kv_heads), exceed what one
+                                  kernel holds (64 at head_dim 128, 32 at 256),
+                                  the queries go in blocks of q_block (each
+                                  block a work list and launches of its own);
+                                  one query's rows must fit, else
+                                  PA_ERR_UNSUPPORTED                         */
   int32_t num_q_heads;
   int32_t num_kv_heads;        /* divides num_q_heads                        */
   int32_t head_dim;            /* 128 or 256                                 */
@@ -121,12 +125,12 @@ typedef struct pa_plan_t {
   pa_dims dims;                /* validated copy, defaults applied           */
   int32_t num_cus;             /* hipDeviceAttributeMultiprocessorCount      */
   int32_t grid;                /* num_cus * grid_multiplier                  */
-  int32_t rows;                /* q_len * (num_q_heads / num_kv_heads)       */
+  int32_t rows;                /* q_block * (num_q_heads / num_kv_heads)     */
   int32_t num_pairs;           /* batch * num_kv_heads                       */
   int32_t max_items;           /* capacity of the item list                  */
   int32_t max_segs;            /* capacity of the segment list (= max slots) */
   int32_t variant;             /* decode kernel instantiation chosen         */
-  int32_t reserved0;
+  int32_t q_block;             /* queries per block (q_len when they fit)    */
   void* workspace;
   uint64_t workspace_bytes;
   /* byte offsets into the workspace (all 256-byte aligned) */
@@ -149,7 +153,9 @@ typedef struct pa_plan_t {
   uint64_t off_wg_head;        /* int32[grid][16]: workgroup w's first
                                   segment, that segment's seg_info record,
                                   its segment range end, then zeros          */
-  uint64_t reserved[2];
+  uint64_t block_bytes;        /* workspace per block: block j's regions are
+                                  at the offsets above plus j * block_bytes  */
+  uint64_t reserved;
 } pa_plan_t;
 
 #define PA_PLAN_MAGIC 0x50414450u

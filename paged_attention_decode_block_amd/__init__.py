@@ -71,7 +71,7 @@ class pa_plan_t(ctypes.Structure):
         ("magic", ctypes.c_uint32), ("device", ctypes.c_int32), ("dims", pa_dims),
         ("num_cus", ctypes.c_int32), ("grid", ctypes.c_int32), ("rows", ctypes.c_int32),
         ("num_pairs", ctypes.c_int32), ("max_items", ctypes.c_int32), ("max_segs", ctypes.c_int32),
-        ("variant", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+        ("variant", ctypes.c_int32), ("q_block", ctypes.c_int32),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_uint64),
         ("off_status", ctypes.c_uint64), ("off_wg_begin", ctypes.c_uint64),
         ("off_wg_seg_begin", ctypes.c_uint64), ("off_items", ctypes.c_uint64),
@@ -79,7 +79,8 @@ class pa_plan_t(ctypes.Structure):
         ("off_seg_base", ctypes.c_uint64), ("off_pseg_base", ctypes.c_uint64),
         ("off_batch_base", ctypes.c_uint64), ("off_partial_lse", ctypes.c_uint64),
         ("off_partial_o", ctypes.c_uint64), ("off_seg_info", ctypes.c_uint64),
-        ("off_wg_head", ctypes.c_uint64), ("reserved", ctypes.c_uint64 * 2),
+        ("off_wg_head", ctypes.c_uint64), ("block_bytes", ctypes.c_uint64),
+        ("reserved", ctypes.c_uint64),
     ]
 
 

@@ -8,6 +8,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
 
@@ -53,7 +54,8 @@ int g_cu_cache[kMaxDevices] = {0};
 // Validates dims and applies defaults into *out. Host-only. need_decode:
 // the rows per kv head must fit a decode instantiation (not for the append,
 // which takes any q_len).
-int check_dims(const pa_dims* in, pa_dims* out, int* variant, bool need_decode = true) {
+int check_dims(const pa_dims* in, pa_dims* out, int* variant, bool need_decode = true,
+               int* q_block = nullptr) {
   if (!in) return fail(PA_ERR_NULL, "dims is NULL");
   pa_dims d = *in;
   if (d.partition_size == 0) d.partition_size = kDefaultPartition;
@@ -86,14 +88,28 @@ int check_dims(const pa_dims* in, pa_dims* out, int* variant, bool need_decode =
   const int64_t capacity = static_cast<int64_t>(d.max_pages_per_seq) * d.page_size;
   if (capacity > (int64_t(1) << 30)) return fail(PA_ERR_DIMS, "max_pages_per_seq * page_size too large");
   const int64_t rows = static_cast<int64_t>(d.q_len) * (d.num_q_heads / d.num_kv_heads);
-  const int v = pa::pick_variant(d.head_dim, d.kv_dtype == PA_KV_FP8_E4M3FN, d.kv_scale_mode,
+  int v = pa::pick_variant(d.head_dim, d.kv_dtype == PA_KV_FP8_E4M3FN, d.kv_scale_mode,
                                  static_cast<int>(rows > 4096 ? 4096 : rows), d.page_size,
                                  d.partition_size);
-  if (need_decode && (rows > 4096 || v < 0))
-    return fail(PA_ERR_UNSUPPORTED,
-                "q_len * (num_q_heads / num_kv_heads) = %lld rows per kv head is more than the "
-                "kernels hold for head_dim %d",
-                static_cast<long long>(rows), d.head_dim);
+  int qb = d.q_len;
+  if (need_decode && (rows > 4096 || v < 0)) {
+    // more rows than one kernel holds: the queries go in blocks of the most
+    // whose rows one does, each block decoded as its own work list
+    const int64_t group = d.num_q_heads / d.num_kv_heads;
+    qb = 0;
+    for (int q = static_cast<int>(std::min<int64_t>(d.q_len, 64)); q >= 1 && qb == 0; --q) {
+      if (q * group > 64) continue;
+      v = pa::pick_variant(d.head_dim, d.kv_dtype == PA_KV_FP8_E4M3FN, d.kv_scale_mode,
+                           static_cast<int>(q * group), d.page_size, d.partition_size);
+      if (v >= 0) qb = q;
+    }
+    if (qb == 0)
+      return fail(PA_ERR_UNSUPPORTED,
+                  "num_q_heads / num_kv_heads = %lld rows of one query are more than the kernels "
+                  "hold for head_dim %d",
+                  static_cast<long long>(group), d.head_dim);
+  }
+  if (q_block) *q_block = qb;
   const int64_t pairs = static_cast<int64_t>(d.batch) * d.num_kv_heads;
   const int64_t items = pairs * ((capacity + d.partition_size - 1) / d.partition_size);
   if (pairs > (1 << 24) || items > (int64_t(1) << 30))
@@ -142,6 +158,30 @@ Layout layout(const pa_dims& d, int num_cus) {
   return L;
 }
 
+// The work list of one block of queries (all of them when they fit one
+// kernel), and the blocks: block j holds queries [j qb, min((j+1) qb, q_len)),
+// each with its own block_bytes of workspace.
+struct Geometry {
+  Layout L;
+  int qb, nblk;
+  uint64_t block_bytes, total;
+};
+
+Geometry geometry(const pa_dims& d, int num_cus, int qb) {
+  Geometry g;
+  pa_dims db = d;
+  db.q_len = qb;
+  g.L = layout(db, num_cus);
+  g.qb = qb;
+  g.nblk = (d.q_len + qb - 1) / qb;
+  g.block_bytes = round256(g.L.total);
+  g.total = g.block_bytes * static_cast<uint64_t>(g.nblk);
+  return g;
+}
+
+int block_q_len(const pa_plan_t* p, int j) { return std::min(p->q_block, p->dims.q_len - j * p->q_block); }
+int num_blocks(const pa_plan_t* p) { return (p->dims.q_len + p->q_block - 1) / p->q_block; }
+
 int current_device(int* dev) {
   const hipError_t e = hipGetDevice(dev);
   if (e != hipSuccess) return fail(PA_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
@@ -189,32 +229,38 @@ int check_decode_args(const pa_plan_t* plan, const void* q, const void* k_cache,
   return check_plan(plan);
 }
 
+// Kernel arguments of query block blk (its queries' rows of q and out, its
+// part of the workspace).
 pa::DecodeArgs decode_args(const pa_plan_t* plan, const void* q, const void* k_cache,
                            const void* v_cache, const int32_t* block_table,
                            const int32_t* context_lens, float scale, const float* kv_scales,
-                           void* out) {
+                           void* out, int blk = 0) {
   const pa_dims& d = plan->dims;
+  const uint64_t wb = plan->block_bytes * static_cast<uint64_t>(blk);
+  const int64_t q0 = static_cast<int64_t>(blk) * plan->q_block * d.num_q_heads * d.head_dim;
+  const int group = d.num_q_heads / d.num_kv_heads;
   pa::DecodeArgs a;
-  a.q = static_cast<const uint16_t*>(q);
+  a.q = static_cast<const uint16_t*>(q) + q0;
   a.k_cache = static_cast<const uint8_t*>(k_cache);
   a.v_cache = static_cast<const uint8_t*>(v_cache);
   a.block_table = block_table;
   a.context_lens = context_lens;
-  a.seg_info = at<const int32_t>(plan, plan->off_seg_info);
-  a.wg_head = at<const int32_t>(plan, plan->off_wg_head);
-  a.nseg = at<const int32_t>(plan, plan->off_nseg);
-  a.seg_base = at<const int32_t>(plan, plan->off_seg_base);
+  a.seg_info = at<const int32_t>(plan, plan->off_seg_info + wb);
+  a.wg_head = at<const int32_t>(plan, plan->off_wg_head + wb);
+  a.nseg = at<const int32_t>(plan, plan->off_nseg + wb);
+  a.seg_base = at<const int32_t>(plan, plan->off_seg_base + wb);
   a.kv_scales = kv_scales;
-  a.out = static_cast<uint16_t*>(out);
-  a.partial_o = at<float>(plan, plan->off_partial_o);
-  a.partial_lse = at<float>(plan, plan->off_partial_lse);
-  a.status = at<int32_t>(plan, plan->off_status);
+  a.out = static_cast<uint16_t*>(out) + q0;
+  a.partial_o = at<float>(plan, plan->off_partial_o + wb);
+  a.partial_lse = at<float>(plan, plan->off_partial_lse + wb);
+  a.status = at<int32_t>(plan, plan->off_status + wb);
   a.batch = d.batch;
-  a.q_len = d.q_len;
+  a.q_len = block_q_len(plan, blk);
+  a.q_total = d.q_len;
   a.num_q_heads = d.num_q_heads;
   a.num_kv_heads = d.num_kv_heads;
-  a.group = d.num_q_heads / d.num_kv_heads;
-  a.rows = plan->rows;
+  a.group = group;
+  a.rows = a.q_len * group;
   a.ps_log2 = log2i(d.page_size);
   a.max_pages = d.max_pages_per_seq;
   a.num_pages = d.num_pages;
@@ -267,18 +313,18 @@ int pa_query_device(int32_t device, int32_t* num_cus) {
 int pa_workspace_bytes(const pa_dims* dims, int32_t num_cus, uint64_t* bytes) {
   if (!bytes) return fail(PA_ERR_NULL, "bytes is NULL");
   pa_dims d;
-  int v = -1;
-  if (int rc = check_dims(dims, &d, &v)) return rc;
+  int v = -1, qb = 0;
+  if (int rc = check_dims(dims, &d, &v, true, &qb)) return rc;
   if (num_cus < 1 || num_cus > 65536) return fail(PA_ERR_DIMS, "num_cus %d out of range", num_cus);
-  *bytes = layout(d, num_cus).total;
+  *bytes = geometry(d, num_cus, qb).total;
   return ok();
 }
 
 int pa_plan(const pa_dims* dims, const int32_t* context_lens, void* workspace,
             uint64_t workspace_bytes, pa_plan_t* plan, void* stream) {
   pa_dims d;
-  int v = -1;
-  if (int rc = check_dims(dims, &d, &v)) return rc;
+  int v = -1, qb = 0;
+  if (int rc = check_dims(dims, &d, &v, true, &qb)) return rc;
   if (!context_lens || !plan) return fail(PA_ERR_NULL, "context_lens and plan are required");
   if (!workspace) return fail(PA_ERR_WORKSPACE, "workspace is NULL");
   if (!aligned(workspace, 256)) return fail(PA_ERR_ALIGN, "workspace must be 256-byte aligned");
@@ -287,11 +333,12 @@ int pa_plan(const pa_dims* dims, const int32_t* context_lens, void* workspace,
   if (int rc = current_device(&dev)) return rc;
   int32_t cus = 0;
   if (int rc = pa_query_device(dev, &cus)) return rc;
-  const Layout L = layout(d, cus);
-  if (workspace_bytes < L.total)
+  const Geometry gm = geometry(d, cus, qb);
+  const Layout& L = gm.L;
+  if (workspace_bytes < gm.total)
     return fail(PA_ERR_WORKSPACE, "workspace of %llu bytes, %llu needed",
                 static_cast<unsigned long long>(workspace_bytes),
-                static_cast<unsigned long long>(L.total));
+                static_cast<unsigned long long>(gm.total));
   pa_plan_t p;
   memset(&p, 0, sizeof(p));
   p.magic = PA_PLAN_MAGIC;
@@ -304,6 +351,8 @@ int pa_plan(const pa_dims* dims, const int32_t* context_lens, void* workspace,
   p.max_items = L.max_items;
   p.max_segs = L.max_segs;
   p.variant = v;
+  p.q_block = gm.qb;
+  p.block_bytes = gm.block_bytes;
   p.workspace = workspace;
   p.workspace_bytes = workspace_bytes;
   p.off_status = L.status;
@@ -320,27 +369,36 @@ int pa_plan(const pa_dims* dims, const int32_t* context_lens, void* workspace,
   p.off_seg_info = L.seg_info;
   p.off_wg_head = L.wg_head;
 
-  pa::PlanArgs a;
-  a.context_lens = context_lens;
-  a.status = at<int32_t>(&p, p.off_status);
-  a.wg_begin = at<int32_t>(&p, p.off_wg_begin);
-  a.wg_seg_begin = at<int32_t>(&p, p.off_wg_seg_begin);
-  a.items = at<pa::Span>(&p, p.off_items);
-  a.segs = at<pa::Span>(&p, p.off_segs);
-  a.nseg = at<int32_t>(&p, p.off_nseg);
-  a.seg_base = at<int32_t>(&p, p.off_seg_base);
-  a.pseg_base = at<int32_t>(&p, p.off_pseg_base);
-  a.batch_base = at<int32_t>(&p, p.off_batch_base);
-  a.seg_info = at<int32_t>(&p, p.off_seg_info);
-  a.wg_head = at<int32_t>(&p, p.off_wg_head);
-  a.batch = d.batch;
-  a.num_kv_heads = d.num_kv_heads;
-  a.q_len = d.q_len;
-  a.partition = d.partition_size;
-  a.grid = L.grid;
-  a.capacity = d.max_pages_per_seq * d.page_size;
-  if (int rc = hip_check(pa::launch_plan(a, L.max_items, static_cast<hipStream_t>(stream)), "plan launch"))
-    return rc;
+  // one work list per block of queries; block j sees the keys up to its
+  // last query, ctx - (q_len - its end) of them
+  for (int j = 0; j < gm.nblk; ++j) {
+    const uint64_t wb = gm.block_bytes * static_cast<uint64_t>(j);
+    const int qj = block_q_len(&p, j);
+    pa::PlanArgs a;
+    a.context_lens = context_lens;
+    a.status = at<int32_t>(&p, p.off_status + wb);
+    a.wg_begin = at<int32_t>(&p, p.off_wg_begin + wb);
+    a.wg_seg_begin = at<int32_t>(&p, p.off_wg_seg_begin + wb);
+    a.items = at<pa::Span>(&p, p.off_items + wb);
+    a.segs = at<pa::Span>(&p, p.off_segs + wb);
+    a.nseg = at<int32_t>(&p, p.off_nseg + wb);
+    a.seg_base = at<int32_t>(&p, p.off_seg_base + wb);
+    a.pseg_base = at<int32_t>(&p, p.off_pseg_base + wb);
+    a.batch_base = at<int32_t>(&p, p.off_batch_base + wb);
+    a.seg_info = at<int32_t>(&p, p.off_seg_info + wb);
+    a.wg_head = at<int32_t>(&p, p.off_wg_head + wb);
+    a.batch = d.batch;
+    a.num_kv_heads = d.num_kv_heads;
+    a.q_len = qj;
+    a.partition = d.partition_size;
+    a.grid = L.grid;
+    a.capacity = d.max_pages_per_seq * d.page_size;
+    a.q_check = d.q_len;
+    a.ctx_offset = d.q_len - (j * gm.qb + qj);
+    if (int rc = hip_check(pa::launch_plan(a, L.max_items, static_cast<hipStream_t>(stream)),
+                           "plan launch"))
+      return rc;
+  }
   *plan = p;
   return ok();
 }
@@ -352,10 +410,15 @@ int pa_decode_partition(const pa_plan_t* plan, const void* q, const void* k_cach
   if (int rc = check_decode_args(plan, q, k_cache, v_cache, block_table, context_lens, q_len,
                                  kv_scale_mode, kv_scales, out))
     return rc;
-  const pa::DecodeArgs a =
-      decode_args(plan, q, k_cache, v_cache, block_table, context_lens, scale, kv_scales, out);
-  return hip_check(pa::launch_partition(plan->variant, a, plan->grid, static_cast<hipStream_t>(stream)),
-                   "partition launch") ?: ok();
+  for (int j = 0; j < num_blocks(plan); ++j) {
+    const pa::DecodeArgs a =
+        decode_args(plan, q, k_cache, v_cache, block_table, context_lens, scale, kv_scales, out, j);
+    if (int rc = hip_check(pa::launch_partition(plan->variant, a, plan->grid,
+                                                static_cast<hipStream_t>(stream)),
+                           "partition launch"))
+      return rc;
+  }
+  return ok();
 }
 
 int pa_decode_reduce(const pa_plan_t* plan, int32_t q_len, int32_t kv_scale_mode, void* out,
@@ -370,10 +433,14 @@ int pa_decode_reduce(const pa_plan_t* plan, int32_t q_len, int32_t kv_scale_mode
   // table's capacity) makes every pair a single item, hence a single
   // segment, written out by the partition pass: nothing is left to merge.
   if (plan->max_items <= plan->num_pairs) return ok();
-  pa::DecodeArgs a = decode_args(plan, out, out, out, nullptr, nullptr, 1.0f, nullptr, out);
-  return hip_check(pa::launch_reduce(a, plan->dims.head_dim, plan->num_pairs,
-                                     static_cast<hipStream_t>(stream)),
-                   "reduce launch") ?: ok();
+  for (int j = 0; j < num_blocks(plan); ++j) {
+    pa::DecodeArgs a = decode_args(plan, out, out, out, nullptr, nullptr, 1.0f, nullptr, out, j);
+    if (int rc = hip_check(pa::launch_reduce(a, plan->dims.head_dim, plan->num_pairs,
+                                             static_cast<hipStream_t>(stream)),
+                           "reduce launch"))
+      return rc;
+  }
+  return ok();
 }
 
 int pa_decode(const pa_plan_t* plan, const void* q, const void* k_cache, const void* v_cache,
@@ -390,12 +457,17 @@ int pa_plan_status(const pa_plan_t* plan, int32_t* device_status, void* stream) 
   if (int rc = check_plan(plan)) return rc;
   if (int rc = hip_check(hipStreamSynchronize(static_cast<hipStream_t>(stream)), "hipStreamSynchronize"))
     return rc;
-  int32_t st = 0;
-  if (int rc = hip_check(hipMemcpy(&st, at<int32_t>(plan, plan->off_status), sizeof(st),
-                                   hipMemcpyDeviceToHost),
-                         "hipMemcpy status"))
-    return rc;
-  *device_status = st;
+  int32_t all = 0;
+  for (int j = 0; j < num_blocks(plan); ++j) {
+    int32_t st = 0;
+    const uint64_t wb = plan->block_bytes * static_cast<uint64_t>(j);
+    if (int rc = hip_check(hipMemcpy(&st, at<int32_t>(plan, plan->off_status + wb), sizeof(st),
+                                     hipMemcpyDeviceToHost),
+                           "hipMemcpy status"))
+      return rc;
+    all |= st;
+  }
+  *device_status = all;
   return ok();
 }
 

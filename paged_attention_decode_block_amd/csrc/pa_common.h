@@ -35,6 +35,8 @@ struct DecodeArgs {
   float* partial_lse;           // [slots][rows]
   int32_t* status;
   int32_t batch, q_len, num_q_heads, num_kv_heads, group, rows;
+  int32_t q_total;               // queries per sequence in q and out; q and out point at this
+                                 // launch's block of q_len of them
   int32_t ps_log2, max_pages, num_pages;
   int32_t scale_mode;           // PA_SCALE_*
   int32_t debug_bounds;

@@ -406,8 +406,9 @@ __device__ __forceinline__ void load_q(const DecodeArgs& a, const Entry& e, int 
                                        bf16x8 (&qr)[RT * (D / 32)]) {
   constexpr int KC = D / 32;
   const int c = lane & 15, j = lane >> 4;
-  const int64_t seq_elems = static_cast<int64_t>(a.q_len) * a.num_q_heads * D;
-  const rsrc_t rq = make_rsrc(a.q + e.b * seq_elems, static_cast<uint32_t>(seq_elems * 2));
+  const int64_t seq_stride = static_cast<int64_t>(a.q_total) * a.num_q_heads * D;
+  const int64_t blk_elems = static_cast<int64_t>(a.q_len) * a.num_q_heads * D;
+  const rsrc_t rq = make_rsrc(a.q + e.b * seq_stride, static_cast<uint32_t>(blk_elems * 2));
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     // rows past R (MFMA padding) reuse the last real row: finite values whose
@@ -788,7 +789,7 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
               const int h = e0.g() * a.group + (r - qi * a.group);
               const f32x8 f8 = {acc0.x, acc0.y, acc0.z, acc0.w, acc1.x, acc1.y, acc1.z, acc1.w};
               const bf16x8 ob8 = __builtin_convertvector(f8, bf16x8);
-              *reinterpret_cast<bf16x8*>(a.out + ((static_cast<int64_t>(e0.b) * a.q_len + qi) *
+              *reinterpret_cast<bf16x8*>(a.out + ((static_cast<int64_t>(e0.b) * a.q_total + qi) *
                                                       a.num_q_heads + h) * D + d0) = ob8;
             } else {
               float* dst = a.partial_o + (static_cast<int64_t>(e0.slot) * pair_rows + r) * D + d0;
@@ -889,7 +890,7 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(DecodeArgs a) {
     const int qi = r / a.group;
     const int h = g * a.group + (r - qi * a.group);
     const f32x8 f8 = {acc0.x, acc0.y, acc0.z, acc0.w, acc1.x, acc1.y, acc1.z, acc1.w};
-    *reinterpret_cast<bf16x8*>(a.out + ((static_cast<int64_t>(b) * a.q_len + qi) * a.num_q_heads + h) *
+    *reinterpret_cast<bf16x8*>(a.out + ((static_cast<int64_t>(b) * a.q_total + qi) * a.num_q_heads + h) *
                                            D + d0) = __builtin_convertvector(f8, bf16x8);
   }
 }

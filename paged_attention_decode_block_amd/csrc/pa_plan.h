@@ -21,6 +21,10 @@ struct PlanArgs {
   int32_t* wg_head;   // [grid][16] (segment begin, first seg_info record, segment end, 0...)
   int32_t batch, num_kv_heads, q_len, partition, grid;
   int32_t capacity;  // max_pages_per_seq * page_size
+  // A block of q_len queries out of q_check per sequence: context lengths
+  // are validated against q_check, and the work list covers the keys the
+  // block sees, ctx - ctx_offset of them (ctx_offset = the queries after it).
+  int32_t q_check, ctx_offset;
 };
 
 // Launches the plan kernel on s; max_items bounds the item count (it sizes

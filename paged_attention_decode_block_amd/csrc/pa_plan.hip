@@ -50,9 +50,10 @@ struct Tables {
   int32_t* sbase;  // [pairs]  first split slot
   int32_t* pbase;  // [pairs]  first segment
   const int32_t* in_ctx;
+  int32_t off;     // ctx_offset, subtracted from the input lengths
   __device__ __forceinline__ int32_t context(int32_t b) const {
     if constexpr (kLds) return ctx[b];
-    return in_ctx[b];
+    return in_ctx[b] - off;
   }
 };
 
@@ -72,9 +73,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   const int32_t pairs = B * H;
   Tables<kLds> t;
   if constexpr (kLds) {
-    t = {l_ctx, l_base, l_nseg, l_sbase, l_pbase, a.context_lens};
+    t = {l_ctx, l_base, l_nseg, l_sbase, l_pbase, a.context_lens, a.ctx_offset};
   } else {
-    t = {nullptr, a.batch_base, a.nseg, a.seg_base, a.pseg_base, a.context_lens};
+    t = {nullptr, a.batch_base, a.nseg, a.seg_base, a.pseg_base, a.context_lens, a.ctx_offset};
   }
   const Div byP(P), byH(H);
   auto items_of = [&](int32_t ctx) { return byP(static_cast<int64_t>(ctx) + P - 1); };
@@ -88,10 +89,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   bool my_bad = false;
   for (int32_t b = b_lo; b < b_hi; ++b) {
     const int32_t c = a.context_lens[b];
-    const bool ok = c >= max(1, a.q_len) && c <= a.capacity;
+    const bool ok = c >= max(1, a.q_check) && c <= a.capacity;
     my_bad |= !ok;
-    if constexpr (kLds) t.ctx[b] = c;
-    sum += ok ? H * items_of(c) : 0;
+    if constexpr (kLds) t.ctx[b] = c - a.ctx_offset;
+    sum += ok ? H * items_of(c - a.ctx_offset) : 0;
   }
   __syncthreads();  // bad = 0 is visible
   if (my_bad) bad = 1;

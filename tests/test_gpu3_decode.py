@@ -207,3 +207,39 @@ def test_pages_beyond_4_gib(kv):
     assert np.array_equal(bits(k_big[base:].cpu()), wk) and np.array_equal(bits(v_big[base:].cpu()), wv)
     if ws is not None:
         assert np.array_equal(sc_big[:, base:].cpu().numpy().view(np.uint32), ws.view(np.uint32))
+
+
+LONG_Q = {
+    # name: (q_len, Hq, Hkv, D, kv dtype, scale mode); rows = q_len * Hq / Hkv
+    "q5_g16_d128": (5, 16, 1, 128, W.KV_BF16, W.SCALE_NONE),           # 80 rows: blocks of 4 + 1
+    "q24_g8_d128": (24, 8, 1, 128, W.KV_BF16, W.SCALE_NONE),           # 192 rows: 3 blocks of 8
+    "q40_g1_d256": (40, 4, 4, 256, W.KV_BF16, W.SCALE_NONE),           # 40 rows: 32 + 8
+    "q8_g16_fp8_tok": (8, 16, 1, 128, W.KV_FP8, W.SCALE_PER_TOKEN_HEAD),  # 128 rows: 2 blocks
+    "q9_g16_fp8_ten": (9, 16, 1, 128, W.KV_FP8, W.SCALE_PER_TENSOR),      # 144 rows: 4 + 4 + 1
+}
+
+
+@pytest.mark.parametrize("name", list(LONG_Q))
+def test_long_queries_in_blocks(name):
+    """More query rows per kv head than one kernel holds: the queries are
+    decoded in blocks, each with the keys up to its own last query (chunked
+    prefill of q_len tokens). Contexts include the shortest, ctx = q_len."""
+    q_len, hq, hkv, d, kvd, mode = LONG_Q[name]
+    ps = 1024 if kvd == W.KV_FP8 else 32
+    spec = W.Spec(name, 4, q_len, hq, hkv, d, ps, q_len, 1500, kv_dtype=kvd, kv_scale_mode=mode,
+                  max_ctx=2048)
+    ctxs = [q_len, q_len + 1, 700, 1500]
+    w = W.generate(spec, 2029, context_lens=ctxs)
+    say(f"[decode] long q {name} ctx={ctxs}")
+    out, plan = run(w)
+    assert plan.c.q_block < q_len
+    assert pa.pa_plan_status(plan) == 0
+    check(w, out, name)
+
+
+def test_long_queries_bad_context_reports():
+    spec = W.Spec("long_q_bad", 2, 9, 16, 1, 128, 32, 9, 300, max_ctx=512)
+    w = W.generate(spec, 2026, context_lens=[9, 300])
+    w.context_lens[0] = 8                            # shorter than q_len
+    out, plan = run(w)
+    assert pa.pa_plan_status(plan) == pa.PA_DEV_BAD_CONTEXT
