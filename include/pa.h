@@ -184,7 +184,11 @@ int pa_workspace_bytes(const pa_dims* dims, int32_t num_cus, uint64_t* bytes);
  * plus, for the decode, each segment as one 32-byte record (off_seg_info)
  * and each workgroup's segment range and first record (off_wg_head),
  * and fills *plan. Invalid context lengths set PA_DEV_BAD_CONTEXT in the
- * device status word and give an empty plan. Asynchronous. Errors:
+ * device status word and give an empty plan. When the queries go in blocks
+ * (see pa_dims.q_len), one such list is built per block, in its own
+ * block_bytes of the workspace, over the keys up to the block's last query
+ * (ctx_b - (q_len - end of the block)); one kernel launch per block.
+ * Asynchronous. Errors:
  * PA_ERR_NULL, PA_ERR_DIMS, PA_ERR_UNSUPPORTED, PA_ERR_SCALE_MODE,
  * PA_ERR_WORKSPACE, PA_ERR_ALIGN, PA_ERR_DEVICE, PA_ERR_HIP. */
 int pa_plan(const pa_dims* dims, const int32_t* context_lens, void* workspace,
@@ -198,8 +202,9 @@ int pa_plan(const pa_dims* dims, const int32_t* context_lens, void* workspace,
  * dequantised as byte value x scale. q_len and kv_scale_mode must equal the
  * plan's; kv_scales must be NULL iff the mode is PA_SCALE_NONE. q, k_cache,
  * v_cache, out and per-token kv_scales must be 16-byte aligned; block_table,
- * context_lens and per-tensor kv_scales 4-byte aligned. Asynchronous. Errors:
- * PA_ERR_NULL, PA_ERR_ALIGN, PA_ERR_PLAN_MISMATCH, PA_ERR_SCALE_MODE,
+ * context_lens and per-tensor kv_scales 4-byte aligned. With query blocks,
+ * each block is decoded in turn (its rows of q and out). Asynchronous.
+ * Errors: PA_ERR_NULL, PA_ERR_ALIGN, PA_ERR_PLAN_MISMATCH, PA_ERR_SCALE_MODE,
  * PA_ERR_HIP. */
 int pa_decode(const pa_plan_t* plan, const void* q, const void* k_cache, const void* v_cache,
               const int32_t* block_table, const int32_t* context_lens, int32_t q_len,
@@ -220,8 +225,8 @@ int pa_decode_partition(const pa_plan_t* plan, const void* q, const void* k_cach
 int pa_decode_reduce(const pa_plan_t* plan, int32_t q_len, int32_t kv_scale_mode, void* out,
                      void* stream);
 
-/* Synchronise `stream` and copy the device status word (PA_DEV_* bits) to
- * *device_status. The only blocking call. Errors: PA_ERR_NULL,
+/* Synchronise `stream` and copy the device status word (PA_DEV_* bits; the
+ * OR over query blocks) to *device_status. The only blocking call. Errors: PA_ERR_NULL,
  * PA_ERR_PLAN_MISMATCH, PA_ERR_HIP. */
 int pa_plan_status(const pa_plan_t* plan, int32_t* device_status, void* stream);
 
