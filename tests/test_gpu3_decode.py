@@ -243,3 +243,19 @@ def test_long_queries_bad_context_reports():
     w.context_lens[0] = 8                            # shorter than q_len
     out, plan = run(w)
     assert pa.pa_plan_status(plan) == pa.PA_DEV_BAD_CONTEXT
+
+
+@pytest.mark.parametrize("P", [16, 256])
+@pytest.mark.parametrize("kv", ["bf16", "fp8_tok"])
+def test_one_sequence_over_every_workgroup(kv, P):
+    """One long sequence and one kv head: its pair is split over every
+    workgroup (P = 16: 1024 items, four per workgroup, 256 segments; P = 256:
+    64 single-item segments), so the reduce merges that many partials."""
+    base = {"bf16": W.Spec("one_pair_bf16", 1, 4, 16, 1, 128, 16, 16384, 16384, max_ctx=16384),
+            "fp8_tok": W.Spec("one_pair_fp8", 1, 4, 16, 1, 128, 1024, 16384, 16384, kv_dtype=W.KV_FP8,
+                              kv_scale_mode=W.SCALE_PER_TOKEN_HEAD, max_ctx=16384)}[kv]
+    w = W.generate(base, 2026)
+    say(f"[decode] one pair over every workgroup {kv} P={P}")
+    out, plan = run(w, partition=P)
+    assert pa.pa_plan_status(plan) == 0
+    check(w, out, f"one pair {kv} P={P}")
