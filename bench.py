@@ -45,6 +45,7 @@ HBM_PEAK_GBS = 8000.0
 HEADLINE = "C3_batched_gqa"
 FLUSH_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "partition_kernel_hbm_traffic_all_workloads.md")
+MFMA_FILE = os.path.join(ROOT, "profiles", "partition_kernel_mfma_busy_all_workloads.md")
 KERNEL_SOURCES = ("pa_decode.hip", "pa_common.h")
 
 
@@ -83,6 +84,25 @@ def recorded_traffic(workload):
     return None
 
 
+def recorded_mfma(workload):
+    """MFMA busy fraction of the partition kernel (rocprofv3 MfmaUtil / 100) and
+    the bf16 MFMA flops one launch executes (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512),
+    from the committed counter summary, or None when there is no record for the
+    workload or the kernel sources have changed since the counters were taken."""
+    digest = kernel_source_digest()
+    try:
+        lines = open(MFMA_FILE).read().splitlines()
+    except OSError:
+        return None
+    for ln in lines:
+        f = ln.split()
+        if len(f) == 5 and f[0] == "mfma" and f[1] == workload:
+            if f[2] != digest:
+                return None
+            return {"busy_frac": round(float(f[3]) / 100, 4), "flops_per_launch": int(f[4])}
+    return None
+
+
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
@@ -112,8 +132,8 @@ def log(msg):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build runs the decode on a single MI355X "
-              f"and has no multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
+        print(f"bench.py measures one GPU: the decode runs on a single MI355X and has no "
+              f"multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -276,7 +296,9 @@ def main():
     parity = None
     if keep and not args.no_cpu_baseline:
         cpu, parity = cpu_baseline(keep, args.cpu_seconds)
-    traffic = recorded_traffic(head) if not args.partition and not args.grid_multiplier else None
+    recorded = not args.partition and not args.grid_multiplier
+    traffic = recorded_traffic(head) if recorded else None
+    mfma = recorded_mfma(head) if recorded else None
     line = {
         "metric": METRIC,
         "value": round(hr["step_GBps"], 2),
@@ -314,6 +336,9 @@ def main():
             "traffic_detail": traffic,
             "bytes_per_launch": hr["kv_bytes"],
             "mean_launch_us": hr["partition_us_mean"],
+            "mfma_busy_frac": mfma["busy_frac"] if mfma else None,
+            "mfma_tflops": (round(mfma["flops_per_launch"] / hr["partition_us_mean"] / 1e6, 2)
+                            if mfma else None),
         },
         "cpu_baseline": cpu,
         "parity_sample": parity,

@@ -1,0 +1,63 @@
+"""Host-side parts of bench.py: the one-GPU guard and the committed counter
+records it reports (HBM traffic and MFMA busy fraction of the partition
+kernel), which count only while the kernel sources hash to the recorded
+digest."""
+import subprocess
+import sys
+from pathlib import Path
+
+import bench
+import workloads as W
+
+ROOT = Path(__file__).resolve().parents[1]
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = subprocess.run([sys.executable, str(ROOT / "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
+
+
+def _records(path, tag):
+    out = {}
+    for ln in Path(path).read_text().splitlines():
+        f = ln.split()
+        if len(f) == 5 and f[0] == tag:
+            out[f[1]] = f
+    return out
+
+
+def test_counter_records_cover_every_benched_workload():
+    for path, tag in ((bench.TRAFFIC_FILE, "traffic"), (bench.MFMA_FILE, "mfma")):
+        recs = _records(path, tag)
+        assert set(recs) == set(W.CONFIGS), (path, sorted(recs))
+        assert bench.HEADLINE in recs
+        digests = {f[2] for f in recs.values()}
+        assert len(digests) == 1 and len(digests.pop()) == 64
+
+
+def test_records_are_dropped_when_the_sources_change(monkeypatch):
+    recs = _records(bench.MFMA_FILE, "mfma")
+    digest = recs[bench.HEADLINE][2]
+    monkeypatch.setattr(bench, "kernel_source_digest", lambda: digest)
+    m = bench.recorded_mfma(bench.HEADLINE)
+    assert m is not None and 0 <= m["busy_frac"] <= 1 and m["flops_per_launch"] > 0
+    t = bench.recorded_traffic(bench.HEADLINE)
+    assert t is None or t["total_bytes"] == t["read_bytes"] + t["written_bytes"]
+    monkeypatch.setattr(bench, "kernel_source_digest", lambda: "0" * 64)
+    assert bench.recorded_mfma(bench.HEADLINE) is None
+    assert bench.recorded_traffic(bench.HEADLINE) is None
+    assert bench.recorded_mfma("no_such_workload") is None
+
+
+def test_mfma_flops_match_the_padded_tile_count():
+    """Executed bf16 MFMA flops per launch (counted on the GPU) = 4 x kv heads
+    x head_dim x the query rows of a kv head rounded up to the 16-row MFMA tile
+    x each sequence's tokens rounded up to the kernel's 32-token step."""
+    recs = _records(bench.MFMA_FILE, "mfma")
+    for name, f in recs.items():
+        s = W.CONFIGS[name]
+        t = int(((W.draw_context_lens(s, 2026) + 31) // 32 * 32).sum())
+        rows = s.q_len * (s.num_q_heads // s.num_kv_heads)
+        padded = -(-rows // 16) * 16
+        assert int(f[4]) == 4 * t * s.num_kv_heads * padded * s.head_dim, name
