@@ -26,6 +26,10 @@ KV-cache append (the write side, pa_cache_append) at a decode-sized shape (C4's
 (HBM-bound), with the same flush and events. `decode_loop` times back-to-back
 decode steps (context bump, append, plan, decode) launched eagerly, replayed
 as one graph per step, and unrolled eight to a graph.
+
+`--scale-sweep` replaces the step bench with a sweep of the partition kernel
+over context lengths scaled 1/8 .. 2x, fitting time = fixed + bytes / rate per
+workload (one JSON line of fits and points).
 """
 from __future__ import annotations
 
@@ -119,6 +123,9 @@ def parse():
     p.add_argument("--no-append", action="store_true", help="skip the KV-cache append timings")
     p.add_argument("--no-loop", action="store_true",
                    help="skip the decode-loop timings (eager vs graph-captured steps)")
+    p.add_argument("--scale-sweep", action="store_true",
+                   help="instead of the step bench: time the partition kernel at context "
+                        "lengths scaled by 1/8 .. 2 and fit time = fixed + bytes / rate")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run one 512 MiB device copy first (a known-size kernel for scaling "
                         "rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -154,6 +161,9 @@ def main():
         def flush():
             torch.sum(flush_src, dim=0, out=flush_dst)
     cus = pa.pa_query_device(0)
+    if args.scale_sweep:
+        scale_sweep(args, flush)
+        return
     if args.calibrate_copy:
         src = torch.ones(1 << 27, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -413,6 +423,92 @@ def append_bench(args, flush):
 # Decode loops timed eagerly and as graphs: workloads and steps per graph
 LOOP_WORKLOADS = ("C1_tiny", "C2_single_seq", "C3_batched_gqa")
 LOOP_STEPS = 8
+
+
+# (workload, context scale factors) of the scale sweep; C5 stops at its own
+# size (twice would need 17 GB of bf16 K/V drawn on the host)
+SWEEP = (("C3_batched_gqa", (0.125, 0.25, 0.5, 1.0, 2.0)),
+         ("C4_fp8_q1_per_token", (0.125, 0.25, 0.5, 1.0, 2.0)),
+         ("C4_fp8_q4_per_token", (0.125, 0.25, 0.5, 1.0, 2.0)),
+         ("C5_long_ctx_d256", (0.125, 0.25, 0.5, 1.0)))
+
+
+def scale_sweep(args, flush):
+    """Partition-kernel time against KV bytes: each workload with its context
+    lengths (range and capacity) scaled by each factor, the rest of its shape
+    unchanged. A least-squares line time = fixed + bytes / rate splits a
+    launch's cost into a per-launch part (dispatch, the dependent fetches
+    before the first K/V bytes, ramp-up and tail, segment merges) and the
+    steady streaming rate. Median of HIP-event samples, read flush before
+    each. Prints one JSON line."""
+    import numpy as np
+    import torch
+
+    import paged_attention_decode_block_amd as pa
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    cus = pa.pa_query_device(0)
+    stream = torch.cuda.current_stream()
+    mode_of = {W.SCALE_NONE: pa.PA_SCALE_NONE, W.SCALE_PER_TENSOR: pa.PA_SCALE_PER_TENSOR,
+               W.SCALE_PER_TOKEN_HEAD: pa.PA_SCALE_PER_TOKEN_HEAD}
+    fits, points = {}, []
+    for name, factors in SWEEP:
+        base = W.CONFIGS[name]
+        xs, ys = [], []
+        for f in factors:
+            hi = int(base.ctx_hi * f)
+            lo = max(int(base.ctx_lo * f), base.q_len)
+            spec = W.scaled(base, ctx_lo=lo, ctx_hi=hi, max_ctx=0)
+            w = W.generate(spec, args.seed)
+            d = {k: getattr(w, k).to(dev) for k in ("q", "k_cache", "v_cache", "block_table",
+                                                     "context_lens")}
+            kvs = None if w.kv_scales is None else w.kv_scales.to(dev)
+            mode = mode_of[spec.kv_scale_mode]
+            dims = pa.make_dims(batch=spec.batch, q_len=spec.q_len, num_q_heads=spec.num_q_heads,
+                                num_kv_heads=spec.num_kv_heads, head_dim=spec.head_dim,
+                                page_size=spec.page_size, num_pages=w.num_pages,
+                                max_pages_per_seq=spec.max_pages_per_seq,
+                                kv_dtype=pa.PA_KV_FP8_E4M3FN if spec.kv_dtype == W.KV_FP8
+                                else pa.PA_KV_BF16,
+                                kv_scale_mode=mode, partition_size=spec.partition_size)
+            ws = torch.empty(pa.pa_workspace_bytes(dims, cus), dtype=torch.uint8, device=dev)
+            out = torch.empty_like(d["q"])
+            plan = pa.pa_plan(dims, d["context_lens"], workspace=ws, stream=stream)
+            ts = []
+            for i in range(args.warmup + args.steps):
+                if flush is not None:
+                    flush()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                pa.pa_decode_partition(plan, d["q"], d["k_cache"], d["v_cache"], d["block_table"],
+                                       d["context_lens"], spec.q_len, spec.scale, mode, kvs, out,
+                                       stream=stream)
+                e1.record(stream)
+                e1.synchronize()
+                if i >= args.warmup:
+                    ts.append(e0.elapsed_time(e1) * 1e3)
+            torch.cuda.synchronize()
+            assert pa.pa_plan_status(plan) == 0, f"{name} x{f}: device status"
+            t = statistics.median(ts)
+            b = w.kv_bytes()
+            xs.append(b)
+            ys.append(t)
+            points.append({"workload": name, "factor": f, "ctx": [lo, hi], "kv_bytes": b,
+                           "partition_us": round(t, 2), "GBps": round(b / t / 1e3, 1)})
+            log(f"sweep {name} x{f}: {b} bytes, {t:.1f} us, {b / t / 1e3:.0f} GB/s")
+            del d, kvs, ws, out, w
+            torch.cuda.empty_cache()
+        A = np.vstack([np.ones(len(xs)), np.asarray(xs, float)]).T
+        (fixed, inv), *_ = np.linalg.lstsq(A, np.asarray(ys, float), rcond=None)
+        rate = 1.0 / inv / 1e3
+        fits[name] = {"fixed_us": round(float(fixed), 2), "steady_GBps": round(float(rate), 1),
+                      "steady_frac_of_peak": round(float(rate) / HBM_PEAK_GBS, 4)}
+        log(f"sweep {name}: fixed {fixed:.1f} us, steady {rate:.0f} GB/s")
+    print(json.dumps({"metric": "partition kernel time vs KV bytes (context lengths scaled)",
+                      "unit": "us", "steps": args.steps, "warmup": args.warmup,
+                      "fits": fits, "points": points}), flush=True)
 
 
 def decode_loop_bench(args):

@@ -61,3 +61,19 @@ def test_mfma_flops_match_the_padded_tile_count():
         rows = s.q_len * (s.num_q_heads // s.num_kv_heads)
         padded = -(-rows // 16) * 16
         assert int(f[4]) == 4 * t * s.num_kv_heads * padded * s.head_dim, name
+
+
+def test_scale_sweep_shapes_are_valid():
+    """Every scaled shape of the sweep keeps q_len <= ctx_lo <= ctx_hi and a
+    block table wide enough for ctx_hi."""
+    for name, factors in bench.SWEEP:
+        base = W.CONFIGS[name]
+        assert 1.0 in factors
+        for f in factors:
+            hi = int(base.ctx_hi * f)
+            lo = max(int(base.ctx_lo * f), base.q_len)
+            s = W.scaled(base, ctx_lo=lo, ctx_hi=hi, max_ctx=0)
+            assert s.q_len <= s.ctx_lo <= s.ctx_hi
+            assert s.max_pages_per_seq * s.page_size >= s.ctx_hi
+            ctx = W.draw_context_lens(s, 2026)
+            assert int(ctx.min()) >= lo and int(ctx.max()) <= hi
