@@ -743,20 +743,21 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
           st_l[wave][16 * rt + c] = v;
         }
       }
-      __syncthreads();
+      // SH: the O tiles overwrite the stream's K/V tiles, which the stream's
+      // other waves may still be reading. Otherwise each wave's O tile takes
+      // its own V tile, whose reads it has issued already (a wave's LDS
+      // accesses complete in order): one barrier per row tile then publishes
+      // maxima, sums and O together.
+      if constexpr (SH) __syncthreads();
       const int pair_rows = a.rows;
-      // rows are merged over the NST waves that hold them: waves s RS + rsub
+      // rows are merged over the NST waves that hold them: waves s RS + rsub;
+      // each wave's O is stored unscaled and weighted by exp2(m_s - M) below
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        float M = neg_inf();
-#pragma unroll
-        for (int s = 0; s < NST; ++s) M = fmaxf(M, st_m[s * RS + rsub][16 * rt + c]);
-        const float Mu = M == neg_inf() ? 0.f : M;
-        const float f = __builtin_amdgcn_exp2f(m[rt] - Mu);
         float* ob = reinterpret_cast<float*>(SH ? sh_buf(stream, 0) + rsub * C::OBYTES : wlds);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
-          *reinterpret_cast<f32x4*>(ob + c * C::OROW + 16 * dt + 4 * j) = o[dt][rt] * f;
+          *reinterpret_cast<f32x4*>(ob + c * C::OROW + 16 * dt + 4 * j) = o[dt][rt];
         __syncthreads();
         constexpr int UNITS = 16 * (D / 8);  // (row, 8 dims) units of one wave's tile
         for (int u = threadIdx.x; u < RS * UNITS; u += C::THREADS) {
@@ -775,11 +776,12 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
 #pragma unroll
             for (int s = 0; s < NST; ++s) {
               const int ww = s * RS + rs;
-              L += st_l[ww][lr] * __builtin_amdgcn_exp2f(st_m[ww][lr] - Mru);
+              const float wgt = __builtin_amdgcn_exp2f(st_m[ww][lr] - Mru);
+              L += st_l[ww][lr] * wgt;
               const uint8_t* obw = SH ? sh_buf(s, 0) + rs * C::OBYTES : lds_waves + ww * C::WBYTES;
               const float* src = reinterpret_cast<const float*>(obw) + row * C::OROW + d0;
-              acc0 += *reinterpret_cast<const f32x4*>(src);
-              acc1 += *reinterpret_cast<const f32x4*>(src + 4);
+              acc0 += *reinterpret_cast<const f32x4*>(src) * wgt;
+              acc1 += *reinterpret_cast<const f32x4*>(src + 4) * wgt;
             }
             const float inv = L > 0.f ? out_f / L : 0.f;
             acc0 *= inv;
