@@ -44,3 +44,29 @@ def test_full_size_sampled_parity(name):
                                 spec.kv_dtype, spec.kv_scale_mode, w.kv_scales)
         err = assert_close(got[b:b + 1], want, tol(spec), f"{name} sequence {b}")
         say(f"[full] {name} sequence {b} (ctx {int(w.context_lens[b])}): max abs err {err:.2e}")
+
+
+# twice the context lengths of three workloads (the largest shapes bench.py's
+# scale sweep times): up to 16384 tokens at C3, 65536 tokens (64 pages of 1024)
+# at C4
+DOUBLED = ["C3_batched_gqa", "C4_fp8_q1_per_token", "C4_fp8_q4_per_token"]
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("name", DOUBLED)
+def test_doubled_contexts_sampled_parity(name):
+    base = W.CONFIGS[name]
+    spec = W.scaled(base, ctx_lo=2 * base.ctx_lo, ctx_hi=2 * base.ctx_hi, max_ctx=0)
+    w = W.generate(spec, 2029)
+    say(f"[full x2] {name}: {spec.batch} sequences, {int(w.context_lens.sum())} tokens, "
+        f"max {int(w.context_lens.max())}")
+    out, plan = run(w)
+    assert pa.pa_plan_status(plan) == 0
+    got = to_f64(out)
+    assert np.isfinite(got).all()
+    for b in _sample(w.context_lens.tolist(), spec.partition_size):
+        want, _ = oracle.decode(w.q[b:b + 1], w.k_cache, w.v_cache, w.block_table[b:b + 1],
+                                w.context_lens[b:b + 1], spec.q_len, spec.scale, spec.page_size,
+                                spec.kv_dtype, spec.kv_scale_mode, w.kv_scales)
+        err = assert_close(got[b:b + 1], want, tol(spec), f"{name} x2 sequence {b}")
+        say(f"[full x2] {name} sequence {b} (ctx {int(w.context_lens[b])}): max abs err {err:.2e}")
