@@ -35,9 +35,18 @@ namespace {
 
 constexpr int kPlanThreads = 512;
 constexpr int kPlanWaves = kPlanThreads / 64;
-constexpr int kLdsSeqs = 4096;   // sequences whose tables fit in LDS
-constexpr int kLdsPairs = 4096;  // pairs whose tables fit in LDS
-constexpr int kPlanMaxBlocks = 64;
+// LDS tables: context and first item per sequence; segment count, first split
+// slot and first segment per pair. Two capacities: 4096 pairs with every
+// table, and as many pairs as the 160 KiB of a gfx950 workgroup hold (less a
+// little for the scan's wave sums) without the segment counts, which are then
+// recomputed by their closed form where needed. The recomputation (a few
+// double-precision reciprocals) costs the small batches about 0.4 us, so they
+// keep the stored counts.
+constexpr int kLdsBytes = 160 * 1024;
+constexpr int kLdsSeqs = 4096;  // sequences whose tables fit in LDS
+constexpr int kLdsPairsBig = ((kLdsBytes - 256) / 4 - (2 * kLdsSeqs + 1)) / 2 / 16 * 16;  // 16336
+constexpr int kLdsPairsSmall = 4096;
+constexpr int kPlanMaxBlocks = 256;
 
 // Per-sequence and per-pair tables: LDS arrays when they fit (kLds), else
 // the workspace arrays of the same meaning (context lengths are then reread
@@ -46,7 +55,7 @@ template <bool kLds>
 struct Tables {
   int32_t* ctx;    // [B]      context length (LDS only)
   int32_t* base;   // [B + 1]  first item of each sequence
-  int32_t* nseg;   // [pairs]
+  int32_t* nseg;   // [pairs]  (absent from the largest LDS tables)
   int32_t* sbase;  // [pairs]  first split slot
   int32_t* pbase;  // [pairs]  first segment
   const int32_t* in_ctx;
@@ -57,13 +66,16 @@ struct Tables {
   }
 };
 
-template <bool kLds>
+// kPairs: pairs the LDS tables hold (0: tables in the workspace)
+template <int kPairs>
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
-  constexpr int NS = kLds ? kLdsSeqs : 1, NP = kLds ? kLdsPairs : 1;
+  constexpr bool kLds = kPairs > 0;
+  constexpr bool kNseg = kPairs <= kLdsPairsSmall;  // segment counts stored (LDS or workspace)
+  constexpr int NS = kLds ? kLdsSeqs : 1, NP = kLds ? kPairs : 1;
   __shared__ int2 wsum[kPlanWaves];
   __shared__ int32_t bad;
   __shared__ int32_t l_ctx[NS], l_base[NS + 1];
-  __shared__ int32_t l_nseg[NP], l_sbase[NP], l_pbase[NP];
+  __shared__ int32_t l_nseg[kNseg ? NP : 1], l_sbase[NP], l_pbase[NP];
   const int tid = threadIdx.x;
   // this block's share of the per-item, per-workgroup and per-table writes
   const int32_t nblk = kLds ? static_cast<int32_t>(gridDim.x) : 1;
@@ -73,7 +85,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   const int32_t pairs = B * H;
   Tables<kLds> t;
   if constexpr (kLds) {
-    t = {l_ctx, l_base, l_nseg, l_sbase, l_pbase, a.context_lens, a.ctx_offset};
+    t = {l_ctx, l_base, kNseg ? l_nseg : nullptr, l_sbase, l_pbase, a.context_lens, a.ctx_offset};
   } else {
     t = {nullptr, a.batch_base, a.nseg, a.seg_base, a.pseg_base, a.context_lens, a.ctx_offset};
   }
@@ -113,6 +125,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     return;
   }
   const Sched sc(N, G);
+  // segments of the pair whose n items start at item A: closed form
+  auto nseg_of = [&](int32_t A, int32_t n) { return sc.seg_index(A + n - 1, A) + 1; };
+  // pair p's segment count: stored, or recomputed (first item A, n items)
+  auto nseg_at = [&](int32_t p, int32_t A, int32_t n) {
+    if constexpr (kNseg) return t.nseg[p];
+    return nseg_of(A, n);
+  };
   {
     int32_t A = first;
     for (int32_t b = b_lo; b < b_hi; ++b) {
@@ -132,9 +151,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     int32_t b = byH(p_lo), g = p_lo - b * H;
     int32_t n = items_of(t.context(b));
     for (int32_t p = p_lo; p < p_hi; ++p) {
-      const int32_t A = t.base[b] + g * n;
-      const int32_t ns = sc.seg_index(A + n - 1, A) + 1;
-      t.nseg[p] = ns;
+      const int32_t ns = nseg_of(t.base[b] + g * n, n);
+      if constexpr (kNseg) t.nseg[p] = ns;
       cnt.x += ns > 1 ? ns : 0;
       cnt.y += ns;
       if (++g == H && p + 1 < p_hi) {
@@ -145,14 +163,20 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   }
   const int2 run0 = block_exclusive_scan2<kPlanWaves>(cnt, wsum, &tot);
   const int32_t slots = tot.x, S = tot.y;
-  {
+  if (p_lo < p_hi) {
     int2 run = run0;
+    int32_t b = byH(p_lo), g = p_lo - b * H;
+    int32_t n = items_of(t.context(b));
     for (int32_t p = p_lo; p < p_hi; ++p) {
-      const int32_t ns = t.nseg[p];
+      const int32_t ns = nseg_at(p, t.base[b] + g * n, n);
       t.sbase[p] = run.x;
       t.pbase[p] = run.y;
       run.x += ns > 1 ? ns : 0;
       run.y += ns;
+      if (++g == H && p + 1 < p_hi) {
+        g = 0;
+        n = items_of(t.context(++b));
+      }
     }
   }
   __syncthreads();
@@ -179,7 +203,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     int32_t k = x0 - bb - g * n;
     int32_t p = b * H + g;
     int32_t A = bb + g * n;
-    int32_t ns = t.nseg[p], sb = t.sbase[p], pb = t.pbase[p];
+    int32_t ns = nseg_at(p, A, n), sb = t.sbase[p], pb = t.pbase[p];
     int32_t w = sc.owner(x0);
     int32_t lo_w = sc.wg_lo(w), hi_w = sc.wg_lo(w + 1);
     int32_t w_A = sc.owner(A);
@@ -229,7 +253,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
           n = items_of(ctx);
         }
         p = b * H + g;
-        ns = t.nseg[p];
+        ns = nseg_at(p, A, n);
         sb = t.sbase[p];
         pb = t.pbase[p];
       }
@@ -254,7 +278,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     const int32_t p = lo * H + g;
     const int32_t j = sc.seg_index(x, A);
     const int32_t last = min(A + n, sc.wg_lo(sc.owner(x) + 1)) - 1;
-    const int32_t ns = t.nseg[p];
+    const int32_t ns = nseg_at(p, A, n);
     r0 = make_int4(lo, g, (x - A) * P, min((last - A + 1) * P, ctx));
     r1 = make_int4(ns > 1 ? t.sbase[p] + j : -1, ctx, p, 0);
     return t.pbase[p] + j;
@@ -288,7 +312,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   if constexpr (kLds) {
     for (int32_t b = gtid; b <= B; b += gstride) a.batch_base[b] = t.base[b];
     for (int32_t p = gtid; p < pairs; p += gstride) {
-      a.nseg[p] = t.nseg[p];
+      if constexpr (kNseg) {
+        a.nseg[p] = t.nseg[p];
+      } else {
+        const int32_t b = byH(p), n = items_of(t.context(b));
+        a.nseg[p] = nseg_of(t.base[b] + (p - b * H) * n, n);
+      }
       a.seg_base[p] = t.sbase[p];
       a.pseg_base[p] = t.pbase[p];
     }
@@ -305,13 +334,17 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
 }  // namespace
 
 hipError_t launch_plan(const PlanArgs& a, int64_t max_items, hipStream_t s) {
-  if (a.batch <= kLdsSeqs && static_cast<int64_t>(a.batch) * a.num_kv_heads <= kLdsPairs) {
+  const int64_t pairs = static_cast<int64_t>(a.batch) * a.num_kv_heads;
+  if (a.batch <= kLdsSeqs && pairs <= kLdsPairsBig) {
     // about two items per thread at the largest possible item count
     const int64_t want = (max_items + 2 * kPlanThreads - 1) / (2 * kPlanThreads);
     const int blocks = static_cast<int>(want < 1 ? 1 : (want > kPlanMaxBlocks ? kPlanMaxBlocks : want));
-    hipLaunchKernelGGL(plan_kernel<true>, dim3(blocks), dim3(kPlanThreads), 0, s, a);
+    if (pairs <= kLdsPairsSmall)
+      hipLaunchKernelGGL(plan_kernel<kLdsPairsSmall>, dim3(blocks), dim3(kPlanThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL(plan_kernel<kLdsPairsBig>, dim3(blocks), dim3(kPlanThreads), 0, s, a);
   } else
-    hipLaunchKernelGGL(plan_kernel<false>, dim3(1), dim3(kPlanThreads), 0, s, a);
+    hipLaunchKernelGGL(plan_kernel<0>, dim3(1), dim3(kPlanThreads), 0, s, a);
   return hipGetLastError();
 }
 
