@@ -36,24 +36,25 @@ namespace {
 constexpr int kPlanThreads = 512;
 constexpr int kPlanWaves = kPlanThreads / 64;
 // LDS tables: context and first item per sequence; segment count, first split
-// slot and first segment per pair. Two capacities: 4096 pairs with every
-// table, and as many pairs as the 160 KiB of a gfx950 workgroup hold (less a
-// little for the scan's wave sums) without the segment counts, which are then
-// recomputed by their closed form where needed. The recomputation (a few
-// double-precision reciprocals) costs the small batches about 0.4 us, so they
-// keep the stored counts.
+// slot and first segment per pair. Two capacities: 4096 sequences and 4096
+// pairs with every table, and as many as the 160 KiB of a gfx950 workgroup
+// hold (less a little for the scan's wave sums) with only the first items and
+// bases: context lengths are then reread from the input (cached after their
+// first pass) and segment counts recomputed by their closed form where
+// needed. The recomputation (a few double-precision reciprocals) costs the
+// small batches about 0.4 us, so they keep every table.
 constexpr int kLdsBytes = 160 * 1024;
-constexpr int kLdsSeqs = 4096;  // sequences whose tables fit in LDS
-constexpr int kLdsPairsBig = ((kLdsBytes - 256) / 4 - (2 * kLdsSeqs + 1)) / 2 / 16 * 16;  // 16336
-constexpr int kLdsPairsSmall = 4096;
+constexpr int kLdsSeqsSmall = 4096, kLdsPairsSmall = 4096;
+constexpr int kLdsSeqsBig = 8192;
+constexpr int kLdsPairsBig = ((kLdsBytes - 256) / 4 - (kLdsSeqsBig + 1)) / 2 / 16 * 16;  // 16336
 constexpr int kPlanMaxBlocks = 256;
 
-// Per-sequence and per-pair tables: LDS arrays when they fit (kLds), else
-// the workspace arrays of the same meaning (context lengths are then reread
-// from the input).
-template <bool kLds>
+// Per-sequence and per-pair tables: LDS arrays when they fit, else the
+// workspace arrays of the same meaning. Context lengths are in LDS only with
+// kCtx; otherwise they are reread from the input.
+template <bool kCtx>
 struct Tables {
-  int32_t* ctx;    // [B]      context length (LDS only)
+  int32_t* ctx;    // [B]      context length (kCtx only)
   int32_t* base;   // [B + 1]  first item of each sequence
   int32_t* nseg;   // [pairs]  (absent from the largest LDS tables)
   int32_t* sbase;  // [pairs]  first split slot
@@ -61,7 +62,7 @@ struct Tables {
   const int32_t* in_ctx;
   int32_t off;     // ctx_offset, subtracted from the input lengths
   __device__ __forceinline__ int32_t context(int32_t b) const {
-    if constexpr (kLds) return ctx[b];
+    if constexpr (kCtx) return ctx[b];
     return in_ctx[b] - off;
   }
 };
@@ -71,10 +72,11 @@ template <int kPairs>
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   constexpr bool kLds = kPairs > 0;
   constexpr bool kNseg = kPairs <= kLdsPairsSmall;  // segment counts stored (LDS or workspace)
-  constexpr int NS = kLds ? kLdsSeqs : 1, NP = kLds ? kPairs : 1;
+  constexpr bool kCtx = kLds && kNseg;               // context lengths in LDS
+  constexpr int NS = !kLds ? 1 : kNseg ? kLdsSeqsSmall : kLdsSeqsBig, NP = kLds ? kPairs : 1;
   __shared__ int2 wsum[kPlanWaves];
   __shared__ int32_t bad;
-  __shared__ int32_t l_ctx[NS], l_base[NS + 1];
+  __shared__ int32_t l_ctx[kCtx ? NS : 1], l_base[NS + 1];
   __shared__ int32_t l_nseg[kNseg ? NP : 1], l_sbase[NP], l_pbase[NP];
   const int tid = threadIdx.x;
   // this block's share of the per-item, per-workgroup and per-table writes
@@ -83,9 +85,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   const int32_t gtid = blk * kPlanThreads + tid, gstride = nblk * kPlanThreads;
   const int32_t B = a.batch, H = a.num_kv_heads, P = a.partition, G = a.grid;
   const int32_t pairs = B * H;
-  Tables<kLds> t;
+  Tables<kCtx> t;
   if constexpr (kLds) {
-    t = {l_ctx, l_base, kNseg ? l_nseg : nullptr, l_sbase, l_pbase, a.context_lens, a.ctx_offset};
+    t = {kCtx ? l_ctx : nullptr, l_base, kNseg ? l_nseg : nullptr, l_sbase, l_pbase, a.context_lens,
+         a.ctx_offset};
   } else {
     t = {nullptr, a.batch_base, a.nseg, a.seg_base, a.pseg_base, a.context_lens, a.ctx_offset};
   }
@@ -103,7 +106,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     const int32_t c = a.context_lens[b];
     const bool ok = c >= max(1, a.q_check) && c <= a.capacity;
     my_bad |= !ok;
-    if constexpr (kLds) t.ctx[b] = c - a.ctx_offset;
+    if constexpr (kCtx) t.ctx[b] = c - a.ctx_offset;
     sum += ok ? H * items_of(c - a.ctx_offset) : 0;
   }
   __syncthreads();  // bad = 0 is visible
@@ -335,11 +338,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
 
 hipError_t launch_plan(const PlanArgs& a, int64_t max_items, hipStream_t s) {
   const int64_t pairs = static_cast<int64_t>(a.batch) * a.num_kv_heads;
-  if (a.batch <= kLdsSeqs && pairs <= kLdsPairsBig) {
+  if (a.batch <= kLdsSeqsBig && pairs <= kLdsPairsBig) {
     // about two items per thread at the largest possible item count
     const int64_t want = (max_items + 2 * kPlanThreads - 1) / (2 * kPlanThreads);
     const int blocks = static_cast<int>(want < 1 ? 1 : (want > kPlanMaxBlocks ? kPlanMaxBlocks : want));
-    if (pairs <= kLdsPairsSmall)
+    if (a.batch <= kLdsSeqsSmall && pairs <= kLdsPairsSmall)
       hipLaunchKernelGGL(plan_kernel<kLdsPairsSmall>, dim3(blocks), dim3(kPlanThreads), 0, s, a);
     else
       hipLaunchKernelGGL(plan_kernel<kLdsPairsBig>, dim3(blocks), dim3(kPlanThreads), 0, s, a);

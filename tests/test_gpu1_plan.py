@@ -74,18 +74,21 @@ def test_plan_configs(name):
 
 
 def test_plan_tables_past_lds():
-    # more sequences (4096) or pairs (16336) than the plan kernel keeps in LDS:
+    # more sequences (8192) or pairs (16336) than the plan kernel keeps in LDS:
     # the tables live in the workspace and one workgroup builds the list
     r = random.Random(7)
-    _plan_case([r.randint(1, 64) for _ in range(5000)], 1, 16, 1, 16, 4, name="5000 sequences")
+    _plan_case([r.randint(1, 64) for _ in range(8193)], 1, 16, 1, 16, 4, name="8193 sequences")
     _plan_case([r.randint(1, 64) for _ in range(2043)], 8, 16, 1, 16, 4, name="16344 pairs")
 
 
 def test_plan_many_pairs_in_lds():
-    # the largest LDS tables (16336 pairs, up to 256 workgroups writing the
-    # list) and a batch of 1024 sequences x 8 kv heads
+    # the larger LDS tables (up to 8192 sequences and 16336 pairs; context
+    # lengths reread, segment counts recomputed; up to 256 workgroups writing
+    # the list) and a batch of 1024 sequences x 8 kv heads
     r = random.Random(8)
     _plan_case([r.randint(1, 64) for _ in range(2042)], 8, 16, 1, 16, 4, name="16336 pairs")
+    _plan_case([r.randint(1, 64) for _ in range(8192)], 1, 16, 1, 16, 4, name="8192 sequences")
+    _plan_case([r.randint(1, 64) for _ in range(5000)], 2, 16, 4, 16, 4, name="5000 sequences, q_len 4")
     _plan_case([r.randint(1, 300) for _ in range(600)], 8, 32, 1, 16, 20, name="4800 pairs")
     _plan_case([r.randint(512, 8192) for _ in range(1024)], 8, 256, 1, 16, 512,
                name="1024 sequences x 8 kv heads")
