@@ -171,8 +171,10 @@ int pa_workspace_bytes(const pa_dims* dims, int32_t num_cus, uint64_t* bytes);
 
 /* Build the persistent work list on the current HIP device ([P3] overview:
  * "metadata scheduler"; code excerpt: grid = CUs x multiplier). Launches one
- * kernel (up to 256 workgroups; one when the batch has more than 8192
- * sequences or 16336 (sequence, kv head) pairs) that reads context_lens (device
+ * kernel (up to 256 workgroups) or, past 8192 sequences or 16336 (sequence,
+ * kv head) pairs, two (one workgroup builds the per-sequence and per-pair
+ * tables in the workspace, then up to 256 write the items) that read
+ * context_lens (device
  * int32[batch]) and writes into `workspace` (device, 256-byte aligned,
  * >= pa_workspace_bytes):
  *   items   for b, then kv head g, then partition k < ceil(ctx_b / P):

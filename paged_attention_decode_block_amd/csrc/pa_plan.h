@@ -25,10 +25,13 @@ struct PlanArgs {
   // are validated against q_check, and the work list covers the keys the
   // block sees, ctx - ctx_offset of them (ctx_offset = the queries after it).
   int32_t q_check, ctx_offset;
+  // Set by launch_plan: the items are written by a second kernel (batches
+  // whose tables live in the workspace), not by the plan kernel.
+  int32_t items_apart;
 };
 
-// Launches the plan kernel on s; max_items bounds the item count (it sizes
-// the grid).
+// Launches the plan kernel on s (and, past the LDS tables, the items kernel
+// after it); max_items bounds the item count (it sizes the grids).
 hipError_t launch_plan(const PlanArgs& a, int64_t max_items, hipStream_t s);
 
 }  // namespace pa

@@ -67,12 +67,104 @@ struct Tables {
   }
 };
 
+// 3. Items [X0, X1) of the list; thread tid writes the run [x0, x1) of them:
+//    each item and the segment it opens. The owning workgroup w (and its
+//    range [lo_w, hi_w)) advances with x. Shared by the plan kernel (tables in
+//    LDS or the workspace) and the items kernel (tables in the workspace).
+template <bool kCtx, bool kNseg>
+__device__ __forceinline__ void write_items(const PlanArgs& a, const Tables<kCtx>& t, const Sched& sc,
+                                            const Div& byP, int32_t N, int32_t X0, int32_t X1,
+                                            int tid) {
+  const int32_t B = a.batch, H = a.num_kv_heads, P = a.partition, G = a.grid;
+  auto items_of = [&](int32_t ctx) { return byP(static_cast<int64_t>(ctx) + P - 1); };
+  auto nseg_at = [&](int32_t p, int32_t A, int32_t n) {
+    if constexpr (kNseg) return t.nseg[p];
+    return sc.seg_index(A + n - 1, A) + 1;
+  };
+  const int32_t per_x = (X1 - X0 + kPlanThreads - 1) / kPlanThreads;
+  const int32_t x0 = min(X1, X0 + tid * per_x), x1 = min(X1, x0 + per_x);
+  if (x0 < x1) {
+    int lo = 0, hi = B;  // largest b with base[b] <= x0
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (t.base[mid] <= x0) lo = mid; else hi = mid;
+    }
+    int32_t b = lo;
+    int32_t ctx = t.context(b);
+    int32_t n = items_of(ctx);
+    const int32_t bb = t.base[b];
+    int32_t g = Div(n)(x0 - bb);
+    int32_t k = x0 - bb - g * n;
+    int32_t p = b * H + g;
+    int32_t A = bb + g * n;
+    int32_t ns = nseg_at(p, A, n), sb = t.sbase[p], pb = t.pbase[p];
+    int32_t w = sc.owner(x0);
+    int32_t lo_w = sc.wg_lo(w), hi_w = sc.wg_lo(w + 1);
+    int32_t w_A = sc.owner(A);
+    for (int32_t x = x0; x < x1; ++x) {
+      while (x >= hi_w) {  // skips empty ranges too
+        ++w;
+        lo_w = hi_w;
+        hi_w = sc.wg_lo(w + 1);
+      }
+      if (x == A) w_A = w;
+      const int32_t j = N >= G ? w - w_A : x - A;
+      Span it;
+      it.pair = p;
+      it.tok_begin = k * P;
+      it.tok_end = min((k + 1) * P, ctx);
+      it.slot = ns > 1 ? sb + j : -1;
+      if (x == A || x == lo_w) {
+        const int32_t last = min(A + n, hi_w) - 1;
+        Span sg = it;
+        sg.tok_end = min((last - A + 1) * P, ctx);
+        a.segs[pb + j] = sg;
+        // the decode's record: everything a segment needs in one 32-byte load
+        int4* si = reinterpret_cast<int4*>(a.seg_info + 8 * static_cast<int64_t>(pb + j));
+        si[0] = make_int4(b, g, sg.tok_begin, sg.tok_end);
+        si[1] = make_int4(sg.slot, ctx, p, 0);
+        if (N >= G && x == lo_w) {
+          // every range is non-empty: this segment opens workgroup w's range
+          int4* h = reinterpret_cast<int4*>(a.wg_head + 16 * static_cast<int64_t>(w));
+          h[0] = make_int4(pb + j, b, g, sg.tok_begin);
+          h[1] = make_int4(sg.tok_end, sg.slot, ctx, p);
+          h[3] = make_int4(0, 0, 0, 0);
+          if (w > 0)
+            reinterpret_cast<int4*>(a.wg_head + 16 * static_cast<int64_t>(w - 1))[2] =
+                make_int4(pb + j, 0, 0, 0);
+          a.wg_begin[w] = x;
+          a.wg_seg_begin[w] = pb + j;
+        }
+      }
+      a.items[x] = it;
+      if (++k == n && x + 1 < x1) {  // next pair: next kv head, or the next sequence
+        k = 0;
+        A += n;
+        if (++g == H) {
+          g = 0;
+          ++b;
+          ctx = t.context(b);
+          n = items_of(ctx);
+        }
+        p = b * H + g;
+        ns = nseg_at(p, A, n);
+        sb = t.sbase[p];
+        pb = t.pbase[p];
+      }
+    }
+  }
+}
+
 // kPairs: pairs the LDS tables hold (0: tables in the workspace)
 template <int kPairs>
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   constexpr bool kLds = kPairs > 0;
-  constexpr bool kNseg = kPairs <= kLdsPairsSmall;  // segment counts stored (LDS or workspace)
-  constexpr bool kCtx = kLds && kNseg;               // context lengths in LDS
+  // segment counts: read back from the small LDS tables; elsewhere
+  // recomputed where needed (cheaper than a dependent global load), but
+  // still written to the workspace
+  constexpr bool kNseg = kLds && kPairs <= kLdsPairsSmall;
+  constexpr bool kStoreNseg = kNseg || !kLds;
+  constexpr bool kCtx = kNseg;  // context lengths in LDS
   constexpr int NS = !kLds ? 1 : kNseg ? kLdsSeqsSmall : kLdsSeqsBig, NP = kLds ? kPairs : 1;
   __shared__ int2 wsum[kPlanWaves];
   __shared__ int32_t bad;
@@ -155,7 +247,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     int32_t n = items_of(t.context(b));
     for (int32_t p = p_lo; p < p_hi; ++p) {
       const int32_t ns = nseg_of(t.base[b] + g * n, n);
-      if constexpr (kNseg) t.nseg[p] = ns;
+      if constexpr (kStoreNseg) t.nseg[p] = ns;
       cnt.x += ns > 1 ? ns : 0;
       cnt.y += ns;
       if (++g == H && p + 1 < p_hi) {
@@ -184,83 +276,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   }
   __syncthreads();
 
-  // 3. this block's items [X0, X1); thread t writes the run [x0, x1) of them:
-  //    each item and the segment it opens. The owning workgroup w (and its
-  //    range [lo_w, hi_w)) advances with x.
-  const Div byBlk(nblk);
-  const int32_t X0 = byBlk(static_cast<int64_t>(blk) * N);
-  const int32_t X1 = byBlk(static_cast<int64_t>(blk + 1) * N);
-  const int32_t per_x = (X1 - X0 + kPlanThreads - 1) / kPlanThreads;
-  const int32_t x0 = min(X1, X0 + tid * per_x), x1 = min(X1, x0 + per_x);
-  if (x0 < x1) {
-    int lo = 0, hi = B;  // largest b with base[b] <= x0
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (t.base[mid] <= x0) lo = mid; else hi = mid;
-    }
-    int32_t b = lo;
-    int32_t ctx = t.context(b);
-    int32_t n = items_of(ctx);
-    const int32_t bb = t.base[b];
-    int32_t g = Div(n)(x0 - bb);
-    int32_t k = x0 - bb - g * n;
-    int32_t p = b * H + g;
-    int32_t A = bb + g * n;
-    int32_t ns = nseg_at(p, A, n), sb = t.sbase[p], pb = t.pbase[p];
-    int32_t w = sc.owner(x0);
-    int32_t lo_w = sc.wg_lo(w), hi_w = sc.wg_lo(w + 1);
-    int32_t w_A = sc.owner(A);
-    for (int32_t x = x0; x < x1; ++x) {
-      while (x >= hi_w) {  // skips empty ranges too
-        ++w;
-        lo_w = hi_w;
-        hi_w = sc.wg_lo(w + 1);
-      }
-      if (x == A) w_A = w;
-      const int32_t j = N >= G ? w - w_A : x - A;
-      Span it;
-      it.pair = p;
-      it.tok_begin = k * P;
-      it.tok_end = min((k + 1) * P, ctx);
-      it.slot = ns > 1 ? sb + j : -1;
-      if (x == A || x == lo_w) {
-        const int32_t last = min(A + n, hi_w) - 1;
-        Span sg = it;
-        sg.tok_end = min((last - A + 1) * P, ctx);
-        a.segs[pb + j] = sg;
-        // the decode's record: everything a segment needs in one 32-byte load
-        int4* si = reinterpret_cast<int4*>(a.seg_info + 8 * static_cast<int64_t>(pb + j));
-        si[0] = make_int4(b, g, sg.tok_begin, sg.tok_end);
-        si[1] = make_int4(sg.slot, ctx, p, 0);
-        if (N >= G && x == lo_w) {
-          // every range is non-empty: this segment opens workgroup w's range
-          int4* h = reinterpret_cast<int4*>(a.wg_head + 16 * static_cast<int64_t>(w));
-          h[0] = make_int4(pb + j, b, g, sg.tok_begin);
-          h[1] = make_int4(sg.tok_end, sg.slot, ctx, p);
-          h[3] = make_int4(0, 0, 0, 0);
-          if (w > 0)
-            reinterpret_cast<int4*>(a.wg_head + 16 * static_cast<int64_t>(w - 1))[2] =
-                make_int4(pb + j, 0, 0, 0);
-          a.wg_begin[w] = x;
-          a.wg_seg_begin[w] = pb + j;
-        }
-      }
-      a.items[x] = it;
-      if (++k == n && x + 1 < x1) {  // next pair: next kv head, or the next sequence
-        k = 0;
-        A += n;
-        if (++g == H) {
-          g = 0;
-          ++b;
-          ctx = t.context(b);
-          n = items_of(ctx);
-        }
-        p = b * H + g;
-        ns = nseg_at(p, A, n);
-        sb = t.sbase[p];
-        pb = t.pbase[p];
-      }
-    }
+  // 3. this block's items, unless the items kernel writes them
+  if (!a.items_apart) {
+    const Div byBlk(nblk);
+    const int32_t X0 = byBlk(static_cast<int64_t>(blk) * N);
+    const int32_t X1 = byBlk(static_cast<int64_t>(blk + 1) * N);
+    write_items<kCtx, kNseg>(a, t, sc, byP, N, X0, X1, tid);
   }
 
   // 4. per workgroup: its item range, its first segment (the one holding item
@@ -334,20 +355,43 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   }
 }
 
+// Items of a batch whose tables live in the workspace, written by
+// plan_kernel<0> just before on the same stream: every workgroup writes its
+// slice of the list. Nothing to do when that kernel found a bad context
+// length (it emptied the list).
+__global__ __launch_bounds__(kPlanThreads) void plan_items_kernel(PlanArgs a) {
+  if (a.status[ST_BITS] != 0) return;
+  const int32_t N = a.batch_base[a.batch];
+  const Sched sc(N, a.grid);
+  const Tables<false> t = {nullptr,    a.batch_base,    a.nseg,       a.seg_base,
+                           a.pseg_base, a.context_lens, a.ctx_offset};
+  const Div byP(a.partition), byBlk(gridDim.x);
+  const int32_t X0 = byBlk(static_cast<int64_t>(blockIdx.x) * N);
+  const int32_t X1 = byBlk(static_cast<int64_t>(blockIdx.x + 1) * N);
+  write_items<false, false>(a, t, sc, byP, N, X0, X1, threadIdx.x);
+}
+
 }  // namespace
 
 hipError_t launch_plan(const PlanArgs& a, int64_t max_items, hipStream_t s) {
   const int64_t pairs = static_cast<int64_t>(a.batch) * a.num_kv_heads;
-  if (a.batch <= kLdsSeqsBig && pairs <= kLdsPairsBig) {
-    // about two items per thread at the largest possible item count
-    const int64_t want = (max_items + 2 * kPlanThreads - 1) / (2 * kPlanThreads);
-    const int blocks = static_cast<int>(want < 1 ? 1 : (want > kPlanMaxBlocks ? kPlanMaxBlocks : want));
-    if (a.batch <= kLdsSeqsSmall && pairs <= kLdsPairsSmall)
-      hipLaunchKernelGGL(plan_kernel<kLdsPairsSmall>, dim3(blocks), dim3(kPlanThreads), 0, s, a);
-    else
-      hipLaunchKernelGGL(plan_kernel<kLdsPairsBig>, dim3(blocks), dim3(kPlanThreads), 0, s, a);
-  } else
-    hipLaunchKernelGGL(plan_kernel<0>, dim3(1), dim3(kPlanThreads), 0, s, a);
+  // about two items per thread at the largest possible item count
+  const int64_t want = (max_items + 2 * kPlanThreads - 1) / (2 * kPlanThreads);
+  const int blocks = static_cast<int>(want < 1 ? 1 : (want > kPlanMaxBlocks ? kPlanMaxBlocks : want));
+  PlanArgs b = a;
+  b.items_apart = 0;
+  if (a.batch <= kLdsSeqsSmall && pairs <= kLdsPairsSmall) {
+    hipLaunchKernelGGL(plan_kernel<kLdsPairsSmall>, dim3(blocks), dim3(kPlanThreads), 0, s, b);
+  } else if (a.batch <= kLdsSeqsBig && pairs <= kLdsPairsBig) {
+    hipLaunchKernelGGL(plan_kernel<kLdsPairsBig>, dim3(blocks), dim3(kPlanThreads), 0, s, b);
+  } else {
+    // one workgroup builds the tables in the workspace, then every workgroup
+    // of the items kernel writes its slice of the list
+    b.items_apart = 1;
+    hipLaunchKernelGGL(plan_kernel<0>, dim3(1), dim3(kPlanThreads), 0, s, b);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    hipLaunchKernelGGL(plan_items_kernel, dim3(blocks), dim3(kPlanThreads), 0, s, b);
+  }
   return hipGetLastError();
 }
 
