@@ -237,6 +237,27 @@ def test_long_queries_in_blocks(name):
     check(w, out, name)
 
 
+def test_long_queries_past_the_plan_lds_tables():
+    """Query blocks over a batch whose plan tables do not fit in LDS (more
+    than 8192 sequences): each block's work list comes from the table kernel
+    and the items kernel. A sample of sequences is compared with the oracle."""
+    spec = W.Spec("long_q_8200", 8200, 5, 16, 1, 128, 32, 5, 64, max_ctx=64, pool_slack=0.0)
+    w = W.generate(spec, 2039)
+    say(f"[decode] long q, {spec.batch} sequences, {int(w.context_lens.sum())} tokens")
+    out, plan = run(w)
+    assert plan.c.q_block < spec.q_len
+    assert pa.pa_plan_status(plan) == 0
+    got = to_f64(out)
+    assert np.isfinite(got).all()
+    ctx = w.context_lens.tolist()
+    for b in sorted({0, 1, 4095, 4096, 8191, 8192, spec.batch - 1, int(np.argmin(ctx)),
+                     int(np.argmax(ctx))}):
+        want, _ = oracle.decode(w.q[b:b + 1], w.k_cache, w.v_cache, w.block_table[b:b + 1],
+                                w.context_lens[b:b + 1], spec.q_len, spec.scale, spec.page_size,
+                                spec.kv_dtype, spec.kv_scale_mode, w.kv_scales)
+        assert_close(got[b:b + 1], want, tol(spec), f"long q sequence {b}")
+
+
 def test_long_queries_bad_context_reports():
     spec = W.Spec("long_q_bad", 2, 9, 16, 1, 128, 32, 9, 300, max_ctx=512)
     w = W.generate(spec, 2026, context_lens=[9, 300])
