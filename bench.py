@@ -29,7 +29,8 @@ as one graph per step, and unrolled eight to a graph.
 
 `--scale-sweep` replaces the step bench with a sweep of the partition kernel
 over context lengths scaled 1/8 .. 2x, fitting time = fixed + bytes / rate per
-workload (one JSON line of fits and points).
+workload (one JSON line of fits and points). `--plan-sweep` times pa_plan
+alone over batch sizes up to 16384 sequences x 8 kv heads.
 """
 from __future__ import annotations
 
@@ -126,6 +127,9 @@ def parse():
     p.add_argument("--scale-sweep", action="store_true",
                    help="instead of the step bench: time the partition kernel at context "
                         "lengths scaled by 1/8 .. 2 and fit time = fixed + bytes / rate")
+    p.add_argument("--plan-sweep", action="store_true",
+                   help="instead of the step bench: time pa_plan alone over batch sizes from "
+                        "64 x 8 to 16384 x 8 (sequences x kv heads)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run one 512 MiB device copy first (a known-size kernel for scaling "
                         "rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -163,6 +167,9 @@ def main():
     cus = pa.pa_query_device(0)
     if args.scale_sweep:
         scale_sweep(args, flush)
+        return
+    if args.plan_sweep:
+        plan_sweep(args, flush)
         return
     if args.calibrate_copy:
         src = torch.ones(1 << 27, dtype=torch.float32, device=dev)
@@ -509,6 +516,58 @@ def scale_sweep(args, flush):
     print(json.dumps({"metric": "partition kernel time vs KV bytes (context lengths scaled)",
                       "unit": "us", "steps": args.steps, "warmup": args.warmup,
                       "fits": fits, "points": points}), flush=True)
+
+
+# (sequences, kv heads) of the plan sweep: the benchmark's batch, the limits of
+# the plan kernel's LDS tables (4096 and 8192 sequences, 4096 and 16336
+# pairs) and batches past them
+PLAN_SWEEP = ((64, 8), (512, 8), (512, 1), (4096, 1), (4097, 1), (1024, 8), (8192, 1),
+              (16384, 1), (4096, 8), (16384, 8))
+
+
+def plan_sweep(args, flush):
+    """pa_plan device time against batch size: context lengths U[512, 8192]
+    (seed 2026), page 16, partition 256, q_len 1, group 4; median of HIP-event
+    samples around the plan alone, read flush before each. Prints one JSON
+    line."""
+    import numpy as np
+    import torch
+
+    import paged_attention_decode_block_amd as pa
+
+    dev = torch.device("cuda:0")
+    cus = pa.pa_query_device(0)
+    stream = torch.cuda.current_stream()
+    rng = np.random.default_rng(args.seed)
+    points = []
+    for B, hkv in PLAN_SWEEP:
+        ctx_np = rng.integers(512, 8193, size=B).astype(np.int32)
+        ctx = torch.from_numpy(ctx_np).to(dev)
+        dims = pa.make_dims(batch=B, q_len=1, num_q_heads=4 * hkv, num_kv_heads=hkv, head_dim=128,
+                            page_size=16, num_pages=B * 512, max_pages_per_seq=512,
+                            kv_dtype=pa.PA_KV_BF16, kv_scale_mode=pa.PA_SCALE_NONE)
+        ws = torch.empty(pa.pa_workspace_bytes(dims, cus), dtype=torch.uint8, device=dev)
+        ts = []
+        for i in range(args.warmup + args.steps):
+            if flush is not None:
+                flush()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            plan = pa.pa_plan(dims, ctx, workspace=ws, stream=stream)
+            e1.record(stream)
+            e1.synchronize()
+            if i >= args.warmup:
+                ts.append(e0.elapsed_time(e1) * 1e3)
+        assert pa.pa_plan_status(plan) == 0, f"plan {B} x {hkv}: device status"
+        t = statistics.median(ts)
+        points.append({"sequences": B, "kv_heads": hkv, "pairs": B * hkv,
+                       "items": int(hkv * ((ctx_np.astype(np.int64) + 255) // 256).sum()),
+                       "plan_us": round(t, 2)})
+        log(f"plan sweep {B} x {hkv}: {t:.1f} us")
+        del ws, ctx
+    print(json.dumps({"metric": "pa_plan time vs batch size", "unit": "us", "steps": args.steps,
+                      "warmup": args.warmup, "points": points}), flush=True)
 
 
 def decode_loop_bench(args):

@@ -77,3 +77,14 @@ def test_scale_sweep_shapes_are_valid():
             assert s.max_pages_per_seq * s.page_size >= s.ctx_hi
             ctx = W.draw_context_lens(s, 2026)
             assert int(ctx.min()) >= lo and int(ctx.max()) <= hi
+
+
+def test_plan_sweep_shapes_are_valid_dims():
+    """Every batch of the plan sweep passes the library's host-side dims
+    checks (no GPU call: the workspace size for 256 CUs)."""
+    import paged_attention_decode_block_amd as pa
+    for B, hkv in bench.PLAN_SWEEP:
+        dims = pa.make_dims(batch=B, q_len=1, num_q_heads=4 * hkv, num_kv_heads=hkv, head_dim=128,
+                            page_size=16, num_pages=B * 512, max_pages_per_seq=512,
+                            kv_dtype=pa.PA_KV_BF16, kv_scale_mode=pa.PA_SCALE_NONE)
+        assert pa.pa_workspace_bytes(dims, 256) > 0
