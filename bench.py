@@ -670,6 +670,18 @@ def decode_loop_bench(args):
     return res
 
 
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None where unreadable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(keep, seconds):
     """The CPU oracle, as it stands, on a bounded sample of the headline
     workload's sequences; its outputs also check the GPU's on that sample."""
@@ -714,7 +726,9 @@ def cpu_baseline(keep, seconds):
            "kind": "oracle",
            "sample": f"{len(done)} sequence decodes ({passes:.2f} passes over the {spec.batch} "
                      f"sequences of the headline workload, {sum(ctx[b] for b in done)} context "
-                     f"tokens, {kv_total} KV bytes), float64 NumPy oracle, {t_total:.1f}s"}
+                     f"tokens, {kv_total} KV bytes), float64 NumPy oracle, {t_total:.1f}s",
+           "oracle_ms_per_sequence": round(1e3 * t_total / max(len(done), 1), 3),
+           "cpu_model": cpu_model()}
     parity = {"sequences_checked": len(set(done)), "max_abs_err": worst,
               "tolerance": "atol = rtol = 8e-3 (bf16 KV)"}
     return cpu, parity

@@ -88,3 +88,8 @@ def test_plan_sweep_shapes_are_valid_dims():
                             page_size=16, num_pages=B * 512, max_pages_per_seq=512,
                             kv_dtype=pa.PA_KV_BF16, kv_scale_mode=pa.PA_SCALE_NONE)
         assert pa.pa_workspace_bytes(dims, 256) > 0
+
+
+def test_cpu_model_is_read_from_proc_cpuinfo():
+    m = bench.cpu_model()
+    assert m is None or (isinstance(m, str) and m)
