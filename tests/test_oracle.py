@@ -74,6 +74,10 @@ def test_worked_example_plans():
         assert pl.nseg == c["nseg"], c["name"]
         assert pl.seg_base == c["seg_base"], c["name"]
         assert pl.status == c["status"], c["name"]
+        assert [list(x) for x in pl.segs] == c["segs"], c["name"]
+        assert pl.wg_seg_begin == c["wg_seg_begin"], c["name"]
+        assert pl.pseg_base == c["pseg_base"], c["name"]
+        assert pl.batch_base == c["batch_base"], c["name"]
 
 
 def test_code_points():

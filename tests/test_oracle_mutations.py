@@ -118,6 +118,39 @@ def test_planted_plan_mistake_is_caught(monkeypatch):
             TP.test_plan_closed_forms_random(s)
 
 
+def _tables_batch_base_per_head(pl, Hkv):
+    # slip: first item of each sequence counted for one kv head only
+    bb = [0]
+    for b in range(len(pl.batch_base) - 1):
+        bb.append(bb[-1] + (pl.batch_base[b + 1] - pl.batch_base[b]) // Hkv)
+    pl.batch_base = bb
+
+
+def _tables_pseg_inclusive(pl, Hkv):
+    # slip: inclusive instead of exclusive prefix sum of the segment counts
+    run, out = 0, []
+    for n in pl.nseg:
+        run += n
+        out.append(run)
+    pl.pseg_base = out + [run]
+
+
+@pytest.mark.parametrize("slip", [_tables_batch_base_per_head, _tables_pseg_inclusive])
+def test_planted_plan_table_mistake_is_caught(slip, monkeypatch):
+    real = oracle.plan
+
+    def mutated(context_lens, num_kv_heads, *a, **kw):
+        pl = real(context_lens, num_kv_heads, *a, **kw)
+        slip(pl, num_kv_heads)
+        return pl
+    monkeypatch.setattr(oracle, "plan", mutated)
+    with pytest.raises(AssertionError):
+        T.test_worked_example_plans()
+    with pytest.raises(AssertionError):
+        for s in range(40):
+            TP.test_plan_closed_forms_random(s)
+
+
 def _encode_ties_away(x):
     # slip: ties rounded away from zero instead of to the even code
     x = np.asarray(x, dtype=np.float64)

@@ -53,6 +53,19 @@ def _check(pl, ctxs, Hkv, P, G):
             used.setdefault(slot, set()).add((p, w))
     assert sorted(used) == list(range(total))
     assert all(len(v) == 1 for v in used.values())
+    # batch_base[b]: the index of sequence b's first item, read off the item
+    # list (pair // Hkv is the sequence); B + 1 entries ending at N
+    B = len(ctxs)
+    first = [None] * B
+    for x, (p, *_rest) in enumerate(pl.items):
+        first[p // Hkv] = x if first[p // Hkv] is None else first[p // Hkv]
+    assert pl.batch_base == first + [N]
+    for b in range(B):
+        assert pl.batch_base[b + 1] - pl.batch_base[b] == Hkv * -(-ctxs[b] // P)
+    # pseg_base[p]: segments of pairs before p, counted in the segment list
+    # (workgroup order is pair order); consecutive differences are nseg
+    assert pl.pseg_base == [sum(1 for s in pl.segs if s[0] < p) for p in range(pairs + 1)]
+    assert all(pl.pseg_base[p + 1] - pl.pseg_base[p] == pl.nseg[p] for p in range(pairs))
     # segments: one per (workgroup, pair) run, tokens contiguous, slots as items
     assert len(pl.segs) == sum(pl.nseg) == pl.pseg_base[-1]
     assert pl.wg_seg_begin[0] == 0 and pl.wg_seg_begin[-1] == len(pl.segs)
