@@ -78,13 +78,18 @@ enum {
 
 /* Bits of the device status word (pa_plan_status). */
 enum {
-  PA_DEV_BAD_CONTEXT = 1,    /* some context_lens[b] outside
+  PA_DEV_BAD_CONTEXT = 1,    /* pa_plan: some context_lens[b] outside
                                 [max(1, q_len), max_pages_per_seq * page_size];
                                 the plan is then empty and decode writes
-                                nothing                                      */
-  PA_DEV_BAD_PAGE = 2        /* a block-table entry outside [0, num_pages)
+                                nothing. pa_decode: some context_lens[b] below
+                                the length the plan was built with or past
+                                max_pages_per_seq * page_size; that sequence
+                                is then decoded over the plan's length       */
+  PA_DEV_BAD_PAGE = 2,       /* a block-table entry outside [0, num_pages)
                                 (checked only with PA_FLAG_DEBUG_BOUNDS; such
                                 tokens are then read as zeros)               */
+  PA_DEV_DEBUG_DEAD_ROW = 4  /* pa_debug_gather only: a row past a segment's
+                                end did not load as zeros                   */
 };
 
 enum { PA_KV_BF16 = 0, PA_KV_FP8_E4M3FN = 1 };
@@ -206,6 +211,16 @@ int pa_plan(const pa_dims* dims, const int32_t* context_lens, void* workspace,
  * v_cache, out and per-token kv_scales must be 16-byte aligned; block_table,
  * context_lens and per-tensor kv_scales 4-byte aligned. With query blocks,
  * each block is decoded in turn (its rows of q and out). Asynchronous.
+ *
+ * Context lengths are read again here, on the device: sequence b is decoded
+ * over its live context_lens[b] keys, not the length pa_plan saw. The plan
+ * only says where a pair's work may split; its last segment runs to the live
+ * length and the causal mask follows it. So one plan serves later decode
+ * steps while every sequence only grows (pa_cache_append, then pa_decode on
+ * the same plan), up to max_pages_per_seq * page_size; re-plan to rebalance
+ * the work. A live length below the plan's, or past that capacity, sets
+ * PA_DEV_BAD_CONTEXT, and that sequence is decoded over the plan's length.
+ *
  * Errors: PA_ERR_NULL, PA_ERR_ALIGN, PA_ERR_PLAN_MISMATCH, PA_ERR_SCALE_MODE,
  * PA_ERR_HIP. */
 int pa_decode(const pa_plan_t* plan, const void* q, const void* k_cache, const void* v_cache,
@@ -232,14 +247,27 @@ int pa_decode_reduce(const pa_plan_t* plan, int32_t q_len, int32_t kv_scale_mode
  * PA_ERR_PLAN_MISMATCH, PA_ERR_HIP. */
 int pa_plan_status(const pa_plan_t* plan, int32_t* device_status, void* stream);
 
-/* Test support: copy the cache rows every (sequence b, kv head g, token
- * t < ctx_b) reads, through the block table with the decode kernel's own
- * page addressing, to k_out / v_out laid out [batch][num_kv_heads]
- * [max_pages_per_seq * page_size][head_dim] (element type of the cache;
- * rows t >= ctx_b are left untouched). Asynchronous. Errors: as pa_decode. */
+/* Test support: the partition pass's own page loader, run alone. For every
+ * segment of the plan (the last query block's, whose keys reach the end of
+ * each context) and every chunk of it, the loader of the plan's decode
+ * instantiation (block-table entries, then 16-byte buffer loads sized to the
+ * segment's live rows) loads the chunk's K and V rows, and per-token scales in
+ * PA_SCALE_PER_TOKEN_HEAD mode, into registers exactly as pa_decode does;
+ * they are written back out in the order the math reads them:
+ *   k_out, v_out  [batch * num_kv_heads][max_pages_per_seq * page_size]
+ *                 [head_dim] elements of the cache's type; row t of pair
+ *                 (b, g) is the row the decode loaded for key t < ctx_b
+ *   scales_out    [2][batch * num_kv_heads][max_pages_per_seq * page_size]
+ *                 float32 (K, then V scales of the same rows); per-token mode
+ *                 only, else may be NULL
+ * Rows t >= ctx_b are not written. Rows a chunk holds past its segment's end
+ * must load as zeros; any that does not sets PA_DEV_DEBUG_DEAD_ROW in the
+ * status word. The context lengths are the live ones, as in pa_decode.
+ * Asynchronous. Errors: as pa_decode. */
 int pa_debug_gather(const pa_plan_t* plan, const void* k_cache, const void* v_cache,
-                    const int32_t* block_table, const int32_t* context_lens, void* k_out,
-                    void* v_out, void* stream);
+                    const int32_t* block_table, const int32_t* context_lens,
+                    const float* kv_scales, void* k_out, void* v_out, float* scales_out,
+                    void* stream);
 
 /* KV-cache append, the write side of the cache the decode reads ([P2]
  * background: K/V live page by page in the paged cache behind the block

@@ -24,6 +24,7 @@ import ctypes
 import os
 from typing import Optional
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -42,6 +43,7 @@ PA_ERR_DEVICE = -9
 
 PA_DEV_BAD_CONTEXT = 1
 PA_DEV_BAD_PAGE = 2
+PA_DEV_DEBUG_DEAD_ROW = 4
 
 PA_KV_BF16 = 0
 PA_KV_FP8_E4M3FN = 1
@@ -107,7 +109,8 @@ def lib() -> ctypes.CDLL:
                                                    ctypes.c_float, i32, vp, vp, vp]),
             "pa_decode_reduce": (ctypes.c_int, [P(pa_plan_t), i32, i32, vp, vp]),
             "pa_plan_status": (ctypes.c_int, [P(pa_plan_t), P(i32), vp]),
-            "pa_debug_gather": (ctypes.c_int, [P(pa_plan_t), vp, vp, vp, vp, vp, vp, vp]),
+            "pa_debug_gather": (ctypes.c_int, [P(pa_plan_t), vp, vp, vp, vp, vp, vp, vp, vp,
+                                               vp]),
             "pa_cache_append": (ctypes.c_int, [P(pa_dims), vp, vp, vp, vp, vp, vp, vp, vp, vp]),
             "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "pa_last_error": (ctypes.c_char_p, []),
@@ -127,6 +130,74 @@ def _check(rc: int) -> None:
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
+
+
+# Element types a buffer may carry (same width, any view of the bits).
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+_FP8 = (torch.uint8, torch.int8, torch.float8_e4m3fn)
+_I32 = (torch.int32,)
+_F32 = (torch.float32,)
+
+
+def _buf(t, name: str, dtypes, shape=None, optional: bool = False) -> Optional[int]:
+    """Device pointer of a tensor argument after the checks that keep the
+    kernels in bounds: an accepted element type, contiguous, and of the
+    expected shape (or, for a shape given as an int, holding exactly that many
+    elements). The device is checked by _on once every argument has passed
+    these. Raises PaError."""
+    if t is None:
+        if optional:
+            return None
+        raise PaError(PA_ERR_NULL, f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise PaError(PA_ERR_DIMS, f"{name} must be a torch.Tensor, not {type(t).__name__}")
+    if t.dtype not in dtypes:
+        raise PaError(PA_ERR_DIMS, f"{name} has dtype {t.dtype}; expected one of "
+                                   f"{', '.join(str(d) for d in dtypes)}")
+    if not t.is_contiguous():
+        raise PaError(PA_ERR_DIMS, f"{name} must be contiguous")
+    if isinstance(shape, int):
+        if t.numel() != shape:
+            raise PaError(PA_ERR_DIMS, f"{name} holds {t.numel()} elements; expected {shape}")
+    elif shape is not None and tuple(t.shape) != tuple(shape):
+        raise PaError(PA_ERR_DIMS, f"{name} has shape {tuple(t.shape)}; expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+def _on(dev: Optional[torch.device], **tensors) -> None:
+    """Every given tensor is a GPU tensor on dev (on one common GPU when dev is
+    None). Raises PaError."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if t.device.type != "cuda" or (dev is not None and t.device != dev):
+            raise PaError(PA_ERR_DEVICE, f"{name} is on {t.device}; expected {dev or 'a GPU'}")
+        dev = t.device
+
+
+def _cache_args(d: pa_dims, k_cache, v_cache, kv_scales, mode: int):
+    """Pointers of the caches and scales for dims d: caches [num_pages, Hkv,
+    page_size, head_dim] (or flat with that many elements), scales [2] per
+    tensor or [2, num_pages, Hkv, page_size] per token."""
+    cdt = _FP8 if d.kv_dtype == PA_KV_FP8_E4M3FN else _BF16
+    cshape = (d.num_pages, d.num_kv_heads, d.page_size, d.head_dim)
+    shape_of = lambda t: cshape if t is not None and t.dim() == 4 else int(np.prod(cshape))  # noqa: E731
+    k = _buf(k_cache, "k_cache", cdt, shape_of(k_cache))
+    v = _buf(v_cache, "v_cache", cdt, shape_of(v_cache))
+    if mode == PA_SCALE_NONE:
+        if kv_scales is not None:
+            raise PaError(PA_ERR_SCALE_MODE, "kv_scales must be None when kv_scale_mode is NONE")
+        return k, v, None
+    if mode == PA_SCALE_PER_TENSOR:
+        return k, v, _buf(kv_scales, "kv_scales", _F32, 2)
+    sshape = (2,) + cshape[:3]
+    return k, v, _buf(kv_scales, "kv_scales", _F32,
+                      sshape if kv_scales is not None and kv_scales.dim() == 4
+                      else int(np.prod(sshape)))
+
+
+def _plan_device(plan: "Plan") -> torch.device:
+    return torch.device("cuda", plan.c.device)
 
 
 def _stream(stream) -> Optional[int]:
@@ -172,34 +243,57 @@ def pa_workspace_bytes(dims: pa_dims, num_cus: int) -> int:
 
 def pa_plan(dims: pa_dims, context_lens: torch.Tensor, workspace: Optional[torch.Tensor] = None,
             stream=None) -> Plan:
+    _buf(context_lens, "context_lens", _I32, (dims.batch,))
+    _on(None, context_lens=context_lens)
     dev = context_lens.device
     if workspace is None:
         nbytes = pa_workspace_bytes(dims, pa_query_device(dev.index or 0))
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    _buf(workspace, "workspace", (torch.uint8,))
+    _on(dev, workspace=workspace)
     c = pa_plan_t()
     _check(lib().pa_plan(ctypes.byref(dims), _ptr(context_lens), _ptr(workspace),
                          workspace.numel(), ctypes.byref(c), _stream(stream)))
     return Plan(c, workspace)
 
 
+def _decode_ptrs(plan: Plan, q, k_cache, v_cache, block_table, context_lens, kv_scale_mode,
+                 kv_scales, out):
+    d = plan.c.dims
+    qshape = (d.batch, d.q_len, d.num_q_heads, d.head_dim)
+    k, v, sc = _cache_args(d, k_cache, v_cache, kv_scales, kv_scale_mode)
+    ptrs = (_buf(q, "q", _BF16, qshape), k, v,
+            _buf(block_table, "block_table", _I32, (d.batch, d.max_pages_per_seq)),
+            _buf(context_lens, "context_lens", _I32, (d.batch,)), sc,
+            _buf(out, "out", _BF16, qshape))
+    _on(_plan_device(plan), q=q, k_cache=k_cache, v_cache=v_cache, block_table=block_table,
+        context_lens=context_lens, kv_scales=kv_scales, out=out)
+    return ptrs
+
+
 def pa_decode(plan: Plan, q, k_cache, v_cache, block_table, context_lens, q_len: int,
               scale: float, kv_scale_mode: int, kv_scales, out, stream=None):
-    _check(lib().pa_decode(ctypes.byref(plan.c), _ptr(q), _ptr(k_cache), _ptr(v_cache),
-                           _ptr(block_table), _ptr(context_lens), q_len, scale, kv_scale_mode,
-                           _ptr(kv_scales), _ptr(out), _stream(stream)))
+    pq, pk, pv, pbt, pctx, psc, pout = _decode_ptrs(plan, q, k_cache, v_cache, block_table,
+                                                    context_lens, kv_scale_mode, kv_scales, out)
+    _check(lib().pa_decode(ctypes.byref(plan.c), pq, pk, pv, pbt, pctx, q_len, scale,
+                           kv_scale_mode, psc, pout, _stream(stream)))
     return out
 
 
 def pa_decode_partition(plan: Plan, q, k_cache, v_cache, block_table, context_lens, q_len: int,
                         scale: float, kv_scale_mode: int, kv_scales, out, stream=None):
-    _check(lib().pa_decode_partition(ctypes.byref(plan.c), _ptr(q), _ptr(k_cache), _ptr(v_cache),
-                                     _ptr(block_table), _ptr(context_lens), q_len, scale,
-                                     kv_scale_mode, _ptr(kv_scales), _ptr(out), _stream(stream)))
+    pq, pk, pv, pbt, pctx, psc, pout = _decode_ptrs(plan, q, k_cache, v_cache, block_table,
+                                                    context_lens, kv_scale_mode, kv_scales, out)
+    _check(lib().pa_decode_partition(ctypes.byref(plan.c), pq, pk, pv, pbt, pctx, q_len, scale,
+                                     kv_scale_mode, psc, pout, _stream(stream)))
     return out
 
 
 def pa_decode_reduce(plan: Plan, q_len: int, kv_scale_mode: int, out, stream=None):
-    _check(lib().pa_decode_reduce(ctypes.byref(plan.c), q_len, kv_scale_mode, _ptr(out),
+    d = plan.c.dims
+    pout = _buf(out, "out", _BF16, (d.batch, d.q_len, d.num_q_heads, d.head_dim))
+    _on(_plan_device(plan), out=out)
+    _check(lib().pa_decode_reduce(ctypes.byref(plan.c), q_len, kv_scale_mode, pout,
                                   _stream(stream)))
     return out
 
@@ -211,19 +305,41 @@ def pa_plan_status(plan: Plan, stream=None) -> int:
 
 
 def pa_debug_gather(plan: Plan, k_cache, v_cache, block_table, context_lens, k_out, v_out,
-                    stream=None):
-    _check(lib().pa_debug_gather(ctypes.byref(plan.c), _ptr(k_cache), _ptr(v_cache),
-                                 _ptr(block_table), _ptr(context_lens), _ptr(k_out), _ptr(v_out),
-                                 _stream(stream)))
+                    kv_scales=None, scales_out=None, stream=None):
+    """The decode's page loader alone (include/pa.h, pa_debug_gather): k_out /
+    v_out [batch * Hkv, max_pages_per_seq * page_size, head_dim] in the cache's
+    element type; scales_out [2, batch * Hkv, same rows] float32 in per-token
+    mode."""
+    d = plan.c.dims
+    mode = d.kv_scale_mode
+    k, v, sc = _cache_args(d, k_cache, v_cache, kv_scales, mode)
+    rows = d.batch * d.num_kv_heads * d.max_pages_per_seq * d.page_size
+    odt = _FP8 if d.kv_dtype == PA_KV_FP8_E4M3FN else _BF16
+    n_out = rows * d.head_dim
+    ptrs = (k, v, _buf(block_table, "block_table", _I32, (d.batch, d.max_pages_per_seq)),
+            _buf(context_lens, "context_lens", _I32, (d.batch,)), sc,
+            _buf(k_out, "k_out", odt, n_out), _buf(v_out, "v_out", odt, n_out),
+            _buf(scales_out, "scales_out", _F32, 2 * rows,
+                 optional=mode != PA_SCALE_PER_TOKEN_HEAD))
+    _on(_plan_device(plan), k_cache=k_cache, v_cache=v_cache, block_table=block_table,
+        context_lens=context_lens, kv_scales=kv_scales, k_out=k_out, v_out=v_out,
+        scales_out=scales_out)
+    _check(lib().pa_debug_gather(ctypes.byref(plan.c), *ptrs, _stream(stream)))
 
 
 def pa_cache_append(dims: pa_dims, new_k, new_v, block_table, context_lens, k_cache, v_cache,
                     kv_scales=None, device_status=None, stream=None):
     """Write the q_len new tokens' K/V rows of every sequence into the paged
     cache (include/pa.h, pa_cache_append)."""
-    _check(lib().pa_cache_append(ctypes.byref(dims), _ptr(new_k), _ptr(new_v), _ptr(block_table),
-                                 _ptr(context_lens), _ptr(k_cache), _ptr(v_cache), _ptr(kv_scales),
-                                 _ptr(device_status), _stream(stream)))
+    nshape = (dims.batch, dims.q_len, dims.num_kv_heads, dims.head_dim)
+    k, v, sc = _cache_args(dims, k_cache, v_cache, kv_scales, dims.kv_scale_mode)
+    ptrs = (_buf(new_k, "new_k", _BF16, nshape), _buf(new_v, "new_v", _BF16, nshape),
+            _buf(block_table, "block_table", _I32, (dims.batch, dims.max_pages_per_seq)),
+            _buf(context_lens, "context_lens", _I32, (dims.batch,)), k, v, sc,
+            _buf(device_status, "device_status", _I32, 1, optional=True))
+    _on(None, context_lens=context_lens, new_k=new_k, new_v=new_v, block_table=block_table,
+        k_cache=k_cache, v_cache=v_cache, kv_scales=kv_scales, device_status=device_status)
+    _check(lib().pa_cache_append(ctypes.byref(dims), *ptrs, _stream(stream)))
 
 
 def pa_status_string(code: int) -> str:

@@ -264,6 +264,8 @@ pa::DecodeArgs decode_args(const pa_plan_t* plan, const void* q, const void* k_c
   a.ps_log2 = log2i(d.page_size);
   a.max_pages = d.max_pages_per_seq;
   a.num_pages = d.num_pages;
+  a.ctx_offset = d.q_len - (blk * plan->q_block + a.q_len);
+  a.capacity = d.max_pages_per_seq * d.page_size;
   a.scale_mode = d.kv_scale_mode;
   a.debug_bounds = (d.flags & PA_FLAG_DEBUG_BOUNDS) ? 1 : 0;
   a.qk_scale_log2 = scale * 1.4426950408889634f;
@@ -472,22 +474,32 @@ int pa_plan_status(const pa_plan_t* plan, int32_t* device_status, void* stream) 
 }
 
 int pa_debug_gather(const pa_plan_t* plan, const void* k_cache, const void* v_cache,
-                    const int32_t* block_table, const int32_t* context_lens, void* k_out,
-                    void* v_out, void* stream) {
+                    const int32_t* block_table, const int32_t* context_lens,
+                    const float* kv_scales, void* k_out, void* v_out, float* scales_out,
+                    void* stream) {
   if (!plan || !k_cache || !v_cache || !block_table || !context_lens || !k_out || !v_out)
-    return fail(PA_ERR_NULL, "every pointer is required");
+    return fail(PA_ERR_NULL, "plan, caches, block_table, context_lens, k_out and v_out are required");
   if (plan->magic != PA_PLAN_MAGIC) return fail(PA_ERR_PLAN_MISMATCH, "plan was not built by pa_plan");
   if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(k_out, 16) || !aligned(v_out, 16))
     return fail(PA_ERR_ALIGN, "caches and outputs must be 16-byte aligned");
-  if (int rc = check_plan(plan)) return rc;
+  if (!aligned(block_table, 4) || !aligned(context_lens, 4))
+    return fail(PA_ERR_ALIGN, "block_table and context_lens must be 4-byte aligned");
   const pa_dims& d = plan->dims;
+  const bool per_tok = d.kv_scale_mode == PA_SCALE_PER_TOKEN_HEAD;
+  if ((d.kv_scale_mode == PA_SCALE_NONE) != (kv_scales == nullptr))
+    return fail(PA_ERR_SCALE_MODE, "kv_scales must be NULL exactly when kv_scale_mode is NONE");
+  if (per_tok && (!scales_out || !aligned(kv_scales, 16) || !aligned(scales_out, 4)))
+    return fail(!scales_out ? PA_ERR_NULL : PA_ERR_ALIGN,
+                "per-token mode needs scales_out (4-byte aligned) and 16-byte aligned kv_scales");
+  if (int rc = check_plan(plan)) return rc;
+  // the last query block's list: its keys reach the end of every context
+  const int last = num_blocks(plan) - 1;
   pa::DecodeArgs a = decode_args(plan, k_cache, k_cache, v_cache, block_table, context_lens, 1.0f,
-                                 nullptr, k_out);
-  const int elt = d.kv_dtype == PA_KV_FP8_E4M3FN ? 1 : 2;
-  return hip_check(pa::launch_gather(a, d.head_dim, elt, d.max_pages_per_seq * d.page_size,
-                                     static_cast<uint8_t*>(k_out), static_cast<uint8_t*>(v_out),
+                                 kv_scales, k_out, last);
+  return hip_check(pa::launch_loader(plan->variant, a, plan->max_segs, static_cast<uint8_t*>(k_out),
+                                     static_cast<uint8_t*>(v_out), per_tok ? scales_out : nullptr,
                                      static_cast<hipStream_t>(stream)),
-                   "gather launch") ?: ok();
+                   "loader launch") ?: ok();
 }
 
 int pa_cache_append(const pa_dims* dims, const void* new_k, const void* new_v,

@@ -38,6 +38,9 @@ struct DecodeArgs {
   int32_t q_total;               // queries per sequence in q and out; q and out point at this
                                  // launch's block of q_len of them
   int32_t ps_log2, max_pages, num_pages;
+  int32_t ctx_offset;           // queries after this launch's block: its keys end at
+                                // context_lens[b] - ctx_offset
+  int32_t capacity;             // max_pages * page size
   int32_t scale_mode;           // PA_SCALE_*
   int32_t debug_bounds;
   float qk_scale_log2;          // softmax scale * log2(e) (* per-tensor K scale)
@@ -66,6 +69,7 @@ struct Variant {
   int waves;
   int stages;
   int one_page;  // every chunk lies in one page: one block-table entry per chunk
+  int shared;    // waves of a chunk stream sharing its K/V tiles in LDS (0: none)
 };
 
 int num_variants();
@@ -76,7 +80,9 @@ int pick_variant(int head_dim, int fp8, int scale_mode, int rows, int page_size,
 
 hipError_t launch_partition(int variant, const DecodeArgs& a, int grid, hipStream_t s);
 hipError_t launch_reduce(const DecodeArgs& a, int head_dim, int num_pairs, hipStream_t s);
-hipError_t launch_gather(const DecodeArgs& a, int head_dim, int elt_bytes, int capacity,
-                         uint8_t* k_out, uint8_t* v_out, hipStream_t s);
+// Test support: the page loader of instantiation `variant` over every chunk
+// of every segment of the plan in `a`, its registers written out row-major.
+hipError_t launch_loader(int variant, const DecodeArgs& a, int max_segs, uint8_t* k_out,
+                         uint8_t* v_out, float* scales_out, hipStream_t s);
 
 }  // namespace pa

@@ -1,6 +1,6 @@
 // Paged-attention decode kernels for gfx950: the persistent partition pass,
-// the log-sum-exp reduce of split pairs, and a debug gather that shares the
-// partition pass's page addressing.
+// the log-sum-exp reduce of split pairs, and (test support) the partition
+// pass's page loader run alone.
 //
 // What the pages fix: the KV cache is read page by page through a block
 // table (Ascend/RecSDK issue #1281, section "背景与优化特性", background);
@@ -58,10 +58,6 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kSlack = 8.f;  // lazy-rescale slack of the running max (log2 units)
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
-
-__device__ __forceinline__ u32x4 ld16(const uint8_t* p) {
-  return *reinterpret_cast<const u32x4*>(p);
-}
 
 // Load of wave-uniform, read-only metadata (segments, context lengths,
 // block-table entries, per-tensor scales) through the constant address space:
@@ -235,9 +231,27 @@ struct Cursor {
 
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 
+// The live context length of sequence b, read at decode time, replaces the
+// plan's snapshot `ctx` of a segment [.., te): the pair's last segment (the
+// one ending at the snapshot) runs to the live length, and every segment's
+// causal bound follows it. Partitions only set where the work may split, so
+// a plan stays valid while sequences grow. A live length below the snapshot
+// or past the block table's capacity is reported, and the snapshot kept.
+__device__ __forceinline__ void live_context(const DecodeArgs& a, int32_t b, int32_t& te,
+                                             int32_t& ctx) {
+  const int32_t raw = ldu(a.context_lens, b);
+  const int32_t live = raw - a.ctx_offset;
+  if (live >= ctx && raw <= a.capacity) {
+    if (te == ctx) te = live;
+    ctx = live;
+  } else {
+    atomicOr(a.status + ST_BITS, PA_DEV_BAD_CONTEXT);
+  }
+}
+
 // Segment record (b, g, tok_begin, tok_end, slot, ctx, pair, 0), one scalar
-// load.
-__device__ __forceinline__ void cursor_set(Cursor& c, const i32x8& r, int wave) {
+// load, then the live context length.
+__device__ __forceinline__ void cursor_set(Cursor& c, const i32x8& r, int wave, const DecodeArgs& a) {
   c.b = r[0];
   c.g = r[1];
   c.tb = r[2];
@@ -245,10 +259,11 @@ __device__ __forceinline__ void cursor_set(Cursor& c, const i32x8& r, int wave) 
   c.slot = r[4];
   c.ctx = r[5];
   c.k = wave;
+  live_context(a, c.b, c.te, c.ctx);
 }
 
 __device__ __forceinline__ void cursor_load(Cursor& c, const DecodeArgs& a, int wave) {
-  cursor_set(c, ldu(reinterpret_cast<const i32x8*>(a.seg_info), c.s), wave);
+  cursor_set(c, ldu(reinterpret_cast<const i32x8*>(a.seg_info), c.s), wave, a);
 }
 
 // With SH every stream takes the same number of entries per segment,
@@ -466,7 +481,7 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
     if (cur.s >= cur.s_end) return;
     cur.live = 1;
     const i32x8 r = {h0[1], h0[2], h0[3], h0[4], h0[5], h0[6], h0[7], 0};
-    cursor_set(cur, r, stream);
+    cursor_set(cur, r, stream, a);
   }
 
   // Softmax scale in the exp2 domain; per-tensor scales are folded in here
@@ -897,26 +912,99 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(DecodeArgs a) {
   }
 }
 
-// Debug gather: rows of every (pair, token < ctx) through the block table,
-// with the partition pass's cache_row() addressing.
-__global__ __launch_bounds__(64) void gather_kernel(DecodeArgs a, int row_bytes, int capacity,
-                                                    uint8_t* k_out, uint8_t* v_out) {
-  const int p = blockIdx.x;
-  const int t = blockIdx.y * 64 + threadIdx.x;
-  const int b = p / a.num_kv_heads;
-  const int g = p - b * a.num_kv_heads;
-  if (t >= a.context_lens[b] || t >= capacity) return;
-  const int32_t page = a.block_table[static_cast<int64_t>(b) * a.max_pages + (t >> a.ps_log2)];
-  if (a.debug_bounds && (page < 0 || page >= a.num_pages)) {
-    atomicOr(a.status + ST_BITS, PA_DEV_BAD_PAGE);
-    return;
+// Test support: the partition pass's own page loader, alone. Workgroup
+// (s, y) takes segment s of the plan (with the live context length, as the
+// partition pass does) and its chunks y, y + gridDim.y, ...; for each it runs
+// load_pages and issue_kv of one instantiation, exactly as a chunk stream
+// entry would, and writes the registers back out in the layout the math
+// reads them in: lane (c, j) holds bytes [64 i + 16 j, +16) of row
+// 16 blk + c of the chunk, and per-token scales of token 16 blk + 4 j + c % 4.
+// Rows t < te go to [pair][t] of k_out / v_out / scales_out; rows past the
+// segment's end must have loaded as zeros, and any that did not set
+// PA_DEV_DEBUG_DEAD_ROW. With shared tiles (SHR waves per stream) wave r of
+// the workgroup loads its share: K (even r) or V (odd r), blocks from
+// (r / 2) * NBL.
+template <int D, bool FP8, int SM, int NB, bool OPC, int SHR>
+__global__ __launch_bounds__(64 * (SHR ? SHR : 1)) void loader_kernel(DecodeArgs a, uint8_t* k_out,
+                                                                      uint8_t* v_out, float* s_out) {
+  constexpr int ROWB = D * (FP8 ? 1 : 2);
+  constexpr int LPB = ROWB / 64;
+  constexpr int TC = 16 * NB;
+  constexpr bool SH = SHR != 0;
+  constexpr int NBL = Stage<D, FP8, NB, SM, SHR>::NBL;
+  const int lane = threadIdx.x & 63;
+  const int rsub = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15, j = lane >> 4;
+  const int32_t seg = blockIdx.x;
+  if (seg >= ldu(a.status, ST_SEGS)) return;
+  const i32x8 r = ldu(reinterpret_cast<const i32x8*>(a.seg_info), seg);
+  int32_t te = r[3], ctx = r[5];
+  live_context(a, r[0], te, ctx);
+  const int64_t base = static_cast<int64_t>(r[6]) * a.capacity;  // pair's first output row
+  const int64_t plane = static_cast<int64_t>(a.batch) * a.num_kv_heads * a.capacity;
+  for (int32_t k = blockIdx.y;; k += gridDim.y) {
+    Entry e;
+    e.tc0 = r[2] + TC * k;
+    if (e.tc0 >= te) break;
+    e.fg = 1 | 8 | (r[1] << 4);
+    e.b = r[0];
+    e.cq = ctx - a.q_len;
+    e.te = te;
+    e.slot = r[4];
+    uint32_t pg[NB];
+    load_pages<NB, OPC>(a, e, pg);
+    Stage<D, FP8, NB, SM, SHR> st = {};
+    issue_kv<D, FP8, NB, SM, OPC, SHR>(a, e, pg, st, lane, rsub);
+    const auto put = [&](uint8_t* out, int blk, const u32x4 (&w)[LPB]) {
+      const int32_t t = e.tc0 + 16 * blk + c;
+      if (t < te) {
+#pragma unroll
+        for (int i = 0; i < LPB; ++i)
+          *reinterpret_cast<u32x4*>(out + (base + t) * ROWB + 64 * i + 16 * j) = w[i];
+      } else {
+        uint32_t any = 0;
+#pragma unroll
+        for (int i = 0; i < LPB; ++i) any |= w[i].x | w[i].y | w[i].z | w[i].w;
+        if (any) atomicOr(a.status + ST_BITS, PA_DEV_DEBUG_DEAD_ROW);
+      }
+    };
+    if constexpr (SH) {
+      uint8_t* const out = (rsub & 1) ? v_out : k_out;
+      const int blk0 = (rsub >> 1) * NBL;
+#pragma unroll
+      for (int b = 0; b < NBL; ++b) put(out, blk0 + b, st.k[b]);
+    } else {
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk) {
+        put(k_out, blk, st.k[blk]);
+        put(v_out, blk, st.v[blk]);
+      }
+    }
+    if constexpr (SM == PA_SCALE_PER_TOKEN_HEAD) {
+      if (rsub == 0 && c < 4) {
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) {
+          const int32_t t = e.tc0 + 16 * blk + 4 * j + c;
+          if (t < te) {
+            s_out[base + t] = st.ks[blk];
+            s_out[plane + base + t] = st.vs[blk];
+          } else if ((__builtin_bit_cast(uint32_t, st.ks[blk]) | __builtin_bit_cast(uint32_t, st.vs[blk])) != 0) {
+            atomicOr(a.status + ST_BITS, PA_DEV_DEBUG_DEAD_ROW);
+          }
+        }
+      }
+    }
   }
-  const uint64_t src = cache_row(page, g, t & ((1 << a.ps_log2) - 1), a.num_kv_heads, a.ps_log2) * row_bytes;
-  const uint64_t dst = (static_cast<uint64_t>(p) * capacity + t) * row_bytes;
-  for (int x = 0; x < row_bytes; x += 16) {
-    *reinterpret_cast<u32x4*>(k_out + dst + x) = ld16(a.k_cache + src + x);
-    *reinterpret_cast<u32x4*>(v_out + dst + x) = ld16(a.v_cache + src + x);
-  }
+}
+
+template <int D, bool FP8, int SM, int NB, bool OPC, int SHR>
+hipError_t launch_loader_t(const DecodeArgs& a, int max_segs, uint8_t* k_out, uint8_t* v_out,
+                           float* s_out, hipStream_t s) {
+  const int chunks = (a.capacity + 16 * NB - 1) / (16 * NB);
+  const dim3 grid(max_segs, chunks < 1024 ? chunks : 1024);
+  hipLaunchKernelGGL((loader_kernel<D, FP8, SM, NB, OPC, SHR>), grid, dim3(64 * (SHR ? SHR : 1)), 0, s,
+                     a, k_out, v_out, s_out);
+  return hipGetLastError();
 }
 
 template <int D, bool FP8, int SM, int RT, int NB, int NW, int NS, int RS, bool OPC, bool SH>
@@ -926,16 +1014,22 @@ hipError_t launch_partition_t(const DecodeArgs& a, int grid, hipStream_t s) {
 }
 
 using LaunchFn = hipError_t (*)(const DecodeArgs&, int, hipStream_t);
+using LoaderFn = hipError_t (*)(const DecodeArgs&, int, uint8_t*, uint8_t*, float*, hipStream_t);
 
 struct VariantEntry {
   Variant v;
   LaunchFn fn;
+  LoaderFn loader;  // the same instantiation's page loader, alone (test support)
 };
 
-#define PA_V(D, F, SM, RT, NB, NW, NS, RS, OPC) \
-  { {D, F, SM, RT * RS, NB, NW, NS, OPC}, launch_partition_t<D, F != 0, SM, RT, NB, NW, NS, RS, OPC != 0, false> }
-#define PA_VS(D, F, SM, RT, NB, NW, NS, RS, OPC) \
-  { {D, F, SM, RT * RS, NB, NW, NS, OPC}, launch_partition_t<D, F != 0, SM, RT, NB, NW, NS, RS, OPC != 0, true> }
+#define PA_V(D, F, SM, RT, NB, NW, NS, RS, OPC)                                                  \
+  {{D, F, SM, RT * RS, NB, NW, NS, OPC, 0},                                                      \
+   launch_partition_t<D, F != 0, SM, RT, NB, NW, NS, RS, OPC != 0, false>,                      \
+   launch_loader_t<D, F != 0, SM, NB, OPC != 0, 0>}
+#define PA_VS(D, F, SM, RT, NB, NW, NS, RS, OPC)                                                 \
+  {{D, F, SM, RT * RS, NB, NW, NS, OPC, RS},                                                     \
+   launch_partition_t<D, F != 0, SM, RT, NB, NW, NS, RS, OPC != 0, true>,                       \
+   launch_loader_t<D, F != 0, SM, NB, OPC != 0, RS>}
 const VariantEntry kVariants[] = {
     // head dim, fp8, scale mode, row tiles per wave, 16-token blocks per
     // chunk, waves, K/V stages, waves per chunk stream, one page per chunk;
@@ -990,12 +1084,9 @@ hipError_t launch_reduce(const DecodeArgs& a, int head_dim, int num_pairs, hipSt
   return hipGetLastError();
 }
 
-hipError_t launch_gather(const DecodeArgs& a, int head_dim, int elt_bytes, int capacity,
-                         uint8_t* k_out, uint8_t* v_out, hipStream_t s) {
-  const int pairs = a.batch * a.num_kv_heads;
-  hipLaunchKernelGGL(gather_kernel, dim3(pairs, (capacity + 63) / 64), dim3(64), 0, s, a,
-                     head_dim * elt_bytes, capacity, k_out, v_out);
-  return hipGetLastError();
+hipError_t launch_loader(int vi, const DecodeArgs& a, int max_segs, uint8_t* k_out,
+                         uint8_t* v_out, float* scales_out, hipStream_t s) {
+  return kVariants[vi].loader(a, max_segs, k_out, v_out, scales_out, s);
 }
 
 }  // namespace pa

@@ -5,6 +5,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import paged_attention_decode_block_amd as pa
 
@@ -136,8 +137,15 @@ def test_decode_argument_errors_before_any_device_call():
     assert L.pa_decode_reduce(ctypes.byref(c), 1, 0, None, None) == pa.PA_ERR_NULL
     st = ctypes.c_int32()
     assert L.pa_plan_status(None, ctypes.byref(st), None) == pa.PA_ERR_NULL
-    assert L.pa_debug_gather(ctypes.byref(c), 0x20000, 0x30000, 0x40000, 0x50000, None, 0x80000,
-                             None) == pa.PA_ERR_NULL
+    # pa_debug_gather(plan, k, v, block_table, ctx, kv_scales, k_out, v_out, scales_out, stream)
+    assert L.pa_debug_gather(ctypes.byref(c), 0x20000, 0x30000, 0x40000, 0x50000, None, None,
+                             0x80000, None, None) == pa.PA_ERR_NULL
+    assert L.pa_debug_gather(ctypes.byref(c), 0x20000, 0x30000, 0x40000, 0x50000, 0x70000,
+                             0x90000, 0x80000, None, None) == pa.PA_ERR_SCALE_MODE
+    assert L.pa_debug_gather(ctypes.byref(f8), 0x20000, 0x30000, 0x40000, 0x50000, 0x70000,
+                             0x90000, 0x80000, None, None) == pa.PA_ERR_NULL
+    assert L.pa_debug_gather(ctypes.byref(c), 0x20000, 0x30000, 0x40000, 0x50000, None,
+                             0x90008, 0x80000, None, None) == pa.PA_ERR_ALIGN
 
 
 def test_status_strings():
@@ -168,3 +176,93 @@ def test_cache_append_argument_errors_before_any_device_call():
     f8 = _dims(kv_dtype=pa.PA_KV_FP8_E4M3FN, kv_scale_mode=pa.PA_SCALE_PER_TOKEN_HEAD)
     assert _append(f8) == pa.PA_ERR_SCALE_MODE
     assert _append(f8, scales=0x70002) == pa.PA_ERR_ALIGN
+
+
+# ---- the Python binding checks tensors before any call reaches the library
+
+
+def _cpu_plan(**kw):
+    """A plan record (never built) with a CPU workspace, for argument checks."""
+    c = _fake_plan(**kw)
+    c.device = 0
+    return pa.Plan(c, torch.empty(0, dtype=torch.uint8))
+
+
+def _decode_tensors(d, **over):
+    t = dict(q=torch.zeros(d.batch, d.q_len, d.num_q_heads, d.head_dim, dtype=torch.bfloat16),
+             k_cache=torch.zeros(d.num_pages, d.num_kv_heads, d.page_size, d.head_dim,
+                                 dtype=torch.bfloat16),
+             block_table=torch.zeros(d.batch, d.max_pages_per_seq, dtype=torch.int32),
+             context_lens=torch.ones(d.batch, dtype=torch.int32),
+             out=torch.zeros(d.batch, d.q_len, d.num_q_heads, d.head_dim, dtype=torch.bfloat16))
+    t["v_cache"] = t["k_cache"].clone()
+    t.update(over)
+    return t
+
+
+def _py_decode(plan, t, mode=pa.PA_SCALE_NONE, scales=None):
+    d = plan.c.dims
+    return pa.pa_decode(plan, t["q"], t["k_cache"], t["v_cache"], t["block_table"],
+                        t["context_lens"], d.q_len, 0.1, mode, scales, t["out"])
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("q", None, pa.PA_ERR_NULL),
+    ("q", "wrong dtype", pa.PA_ERR_DIMS),
+    ("q", "wrong shape", pa.PA_ERR_DIMS),
+    ("out", "transposed", pa.PA_ERR_DIMS),
+    ("k_cache", "fewer pages", pa.PA_ERR_DIMS),
+    ("k_cache", "flat, one row short", pa.PA_ERR_DIMS),
+    ("block_table", "int64", pa.PA_ERR_DIMS),
+    ("block_table", "short rows", pa.PA_ERR_DIMS),
+    ("context_lens", "wrong batch", pa.PA_ERR_DIMS),
+    ("q", "cpu", pa.PA_ERR_DEVICE),
+])
+def test_binding_rejects_bad_tensors(field, value, code):
+    plan = _cpu_plan(batch=2, q_len=1, max_pages_per_seq=8)
+    d = plan.c.dims
+    good = _decode_tensors(d)
+    bad = {
+        None: None,
+        "wrong dtype": good["q"].float(),
+        "wrong shape": good["q"][:, :, :8],
+        "transposed": good["out"].transpose(2, 3).contiguous().transpose(2, 3),
+        "fewer pages": good["k_cache"][:-1],
+        "flat, one row short": good["k_cache"].flatten()[:-d.head_dim],
+        "int64": good["block_table"].long(),
+        "short rows": good["block_table"][:, :-1].contiguous(),
+        "wrong batch": good["context_lens"][:1],
+        "cpu": good["q"],
+    }[value]
+    with pytest.raises(pa.PaError) as e:
+        _py_decode(plan, dict(good, **{field: bad}))
+    assert e.value.code == code, e.value.text
+
+
+def test_binding_rejects_scales_that_disagree_with_the_mode():
+    f8 = _cpu_plan(kv_dtype=pa.PA_KV_FP8_E4M3FN, kv_scale_mode=pa.PA_SCALE_PER_TOKEN_HEAD)
+    d = f8.c.dims
+    t = _decode_tensors(d, k_cache=torch.zeros(d.num_pages, 1, d.page_size, d.head_dim,
+                                               dtype=torch.uint8))
+    t["v_cache"] = t["k_cache"].clone()
+    with pytest.raises(pa.PaError) as e:       # per-token scales of the wrong shape
+        _py_decode(f8, t, pa.PA_SCALE_PER_TOKEN_HEAD, torch.zeros(2, dtype=torch.float32))
+    assert e.value.code == pa.PA_ERR_DIMS
+    with pytest.raises(pa.PaError) as e:       # bf16 caches for an fp8 plan
+        _py_decode(f8, _decode_tensors(d), pa.PA_SCALE_PER_TOKEN_HEAD,
+                   torch.zeros(2, d.num_pages, 1, d.page_size, dtype=torch.float32))
+    assert e.value.code == pa.PA_ERR_DIMS
+    bf = _cpu_plan()
+    with pytest.raises(pa.PaError) as e:       # scales with a bf16 cache
+        _py_decode(bf, _decode_tensors(bf.c.dims), pa.PA_SCALE_NONE,
+                   torch.ones(2, dtype=torch.float32))
+    assert e.value.code == pa.PA_ERR_SCALE_MODE
+
+
+def test_binding_rejects_host_context_lens_before_planning():
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_plan(_dims(), torch.ones(2, dtype=torch.int32))
+    assert e.value.code == pa.PA_ERR_DEVICE
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_plan(_dims(), torch.ones(3, dtype=torch.int32))
+    assert e.value.code == pa.PA_ERR_DIMS

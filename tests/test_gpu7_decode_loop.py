@@ -186,3 +186,90 @@ def test_graph_captured_decode_loop(name):
                         None if sc is None else torch.from_numpy(sc), loop.start.num_pages)
         check(wi, outs[i], f"{name} step {i}")
     say(f"[loop] {name} ok")
+
+
+@pytest.mark.parametrize("name", list(LOOPS))
+def test_plan_reused_across_steps(name):
+    """One plan, built at the loop's start lengths, serves every step: each
+    step grows context_lens by q_len, appends its tokens and decodes on the
+    same plan, whose pairs' last segments then run to the live lengths
+    (across page and partition boundaries: 254 -> 258 at page 16 and
+    partition 256, 1022 -> 1026 and 1014 -> 1030 at page and partition 1024,
+    488 -> 520 at partition 512). Every step matches the oracle; the same
+    steps replayed from one captured graph (no plan inside) are bitwise
+    equal to the eager ones."""
+    spec, final = LOOPS[name]
+    loop = W.decode_loop(spec, 2026, STEPS, final)
+    s = spec
+    say(f"[reuse] {name} start ctx={loop.start.context_lens.tolist()} steps={STEPS}")
+    dims = dims_for(loop.start)
+    q = loop.q.to(DEV)
+    nk, nv = loop.new_k.to(DEV), loop.new_v.to(DEV)
+    mode = MODE_CODE[s.kv_scale_mode]
+
+    def step(st: State, plan, qi, nki, nvi, out):
+        d = st.d
+        d.context_lens.add_(s.q_len)
+        pa.pa_cache_append(dims, nki, nvi, d.block_table, d.context_lens, d.k_cache, d.v_cache,
+                           d.kv_scales, st.status)
+        pa.pa_decode(plan, qi, d.k_cache, d.v_cache, d.block_table, d.context_lens, s.q_len,
+                     s.scale, mode, d.kv_scales, out)
+
+    eager = State(loop)
+    plan = pa.pa_plan(dims, eager.d.context_lens.clone(), workspace=_workspace(dims))
+    outs = torch.zeros(STEPS, *q.shape[1:], dtype=torch.bfloat16, device=DEV)
+    for i in range(STEPS):
+        step(eager, plan, q[i], nk[i], nv[i], outs[i])
+    torch.cuda.synchronize()
+    assert int(eager.status.item()) == 0 and pa.pa_plan_status(plan) == 0
+
+    g = State(loop)
+    plan_g = pa.pa_plan(dims, g.d.context_lens.clone(), workspace=_workspace(dims))
+    q_in, nk_in, nv_in = q[0].clone(), nk[0].clone(), nv[0].clone()
+    out_g = torch.zeros_like(q[0])
+    graph = _capture(lambda: step(g, plan_g, q_in, nk_in, nv_in, out_g))
+    for i in range(STEPS):
+        q_in.copy_(q[i])
+        nk_in.copy_(nk[i])
+        nv_in.copy_(nv[i])
+        out_g.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g.view(torch.int16), outs[i].view(torch.int16)), f"replay {i}"
+    assert pa.pa_plan_status(plan_g) == 0
+
+    states = _oracle_states(loop)
+    fp8 = s.kv_dtype == W.KV_FP8
+    for i in range(STEPS):
+        kc, vc, sc = states[i]
+        wi = W.Workload(s, 2026, loop.q[i], _as_cache(kc, fp8), _as_cache(vc, fp8),
+                        loop.start.block_table, loop.context_lens_at(i),
+                        None if sc is None else torch.from_numpy(sc), loop.start.num_pages)
+        check(wi, outs[i], f"{name} reused plan, step {i}")
+    say(f"[reuse] {name} ok")
+
+
+def test_stale_plan_is_reported():
+    """Context lengths below the plan's, or past the block table's capacity,
+    set PA_DEV_BAD_CONTEXT, and those sequences are decoded over the plan's
+    lengths: bitwise the output of a decode at the plan's lengths."""
+    spec = W.scaled(W.C3, batch=3, ctx_lo=100, ctx_hi=900, max_ctx=1024)
+    w = W.generate(spec, 2039)
+    d = upload(w)
+    dims = dims_for(w)
+    want = torch.empty_like(d.q)
+    plan = pa.pa_plan(dims, d.context_lens)
+    pa.pa_decode(plan, d.q, d.k_cache, d.v_cache, d.block_table, d.context_lens, 1, spec.scale,
+                 pa.PA_SCALE_NONE, None, want)
+    assert pa.pa_plan_status(plan) == 0
+    cap = spec.max_pages_per_seq * spec.page_size
+    for label, change in (("shrunk", lambda c: c - 5), ("past capacity", lambda c: c * 0 + cap + 3)):
+        live = d.context_lens.clone()
+        live[1] = change(live[1])
+        say(f"[reuse] stale plan: {label}, ctx {d.context_lens.tolist()} -> {live.tolist()}")
+        plan = pa.pa_plan(dims, d.context_lens)
+        out = torch.empty_like(d.q)
+        pa.pa_decode(plan, d.q, d.k_cache, d.v_cache, d.block_table, live, 1, spec.scale,
+                     pa.PA_SCALE_NONE, None, out)
+        assert pa.pa_plan_status(plan) == pa.PA_DEV_BAD_CONTEXT, label
+        assert torch.equal(out.view(torch.int16), want.view(torch.int16)), label
