@@ -300,6 +300,29 @@ int pa_cache_append(const pa_dims* dims, const void* new_k, const void* new_v,
                     const int32_t* block_table, const int32_t* context_lens, void* k_cache,
                     void* v_cache, float* kv_scales, int32_t* device_status, void* stream);
 
+/* pa_plan followed by pa_decode, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. The caller passes inputs and outputs only; the work list
+ * and split partials live in a static scratch array of
+ * pa_static_scratch_bytes() (32 MiB) that the library holds on each device it
+ * runs on until the process ends. Nothing is allocated or freed: no hipMalloc,
+ * no hipFree, no allocating library call. Arguments are those of pa_plan
+ * (dims, context_lens) and pa_decode (the rest), with the same layouts and
+ * errors; a problem whose workspace (pa_workspace_bytes) exceeds the scratch
+ * is rejected with PA_ERR_WORKSPACE before any launch. If plan_out is not
+ * NULL it receives the plan, which points into the scratch (for
+ * pa_plan_status) and stays valid only until the next pa_decode_static call
+ * on that device. Every call on one device shares that device's scratch:
+ * calls that overlap on one device (two streams, or two host threads)
+ * race and must be ordered by the caller. Asynchronous. */
+int pa_decode_static(const pa_dims* dims, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_table, const int32_t* context_lens, int32_t q_len,
+                     float scale, int32_t kv_scale_mode, const float* kv_scales, void* out,
+                     pa_plan_t* plan_out, void* stream);
+
+/* Size in bytes of pa_decode_static's per-device scratch. */
+uint64_t pa_static_scratch_bytes(void);
+
 /* Static text for a PA_* status code. */
 const char* pa_status_string(int status);
 

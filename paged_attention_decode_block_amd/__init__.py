@@ -112,6 +112,9 @@ def lib() -> ctypes.CDLL:
             "pa_debug_gather": (ctypes.c_int, [P(pa_plan_t), vp, vp, vp, vp, vp, vp, vp, vp,
                                                vp]),
             "pa_cache_append": (ctypes.c_int, [P(pa_dims), vp, vp, vp, vp, vp, vp, vp, vp, vp]),
+            "pa_decode_static": (ctypes.c_int, [P(pa_dims), vp, vp, vp, vp, vp, i32,
+                                                ctypes.c_float, i32, vp, vp, P(pa_plan_t), vp]),
+            "pa_static_scratch_bytes": (u64, []),
             "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "pa_last_error": (ctypes.c_char_p, []),
         }
@@ -296,6 +299,30 @@ def pa_decode_reduce(plan: Plan, q_len: int, kv_scale_mode: int, out, stream=Non
     _check(lib().pa_decode_reduce(ctypes.byref(plan.c), q_len, kv_scale_mode, pout,
                                   _stream(stream)))
     return out
+
+
+def pa_decode_static(dims: pa_dims, q, k_cache, v_cache, block_table, context_lens, q_len: int,
+                     scale: float, kv_scale_mode: int, kv_scales, out, stream=None) -> Plan:
+    """pa_plan + pa_decode in the library's static scratch (include/pa.h,
+    pa_decode_static): nothing is allocated. Returns the plan (its workspace
+    is the scratch, valid until the next call on the device) for
+    pa_plan_status."""
+    qshape = (dims.batch, dims.q_len, dims.num_q_heads, dims.head_dim)
+    k, v, sc = _cache_args(dims, k_cache, v_cache, kv_scales, kv_scale_mode)
+    ptrs = (_buf(q, "q", _BF16, qshape), k, v,
+            _buf(block_table, "block_table", _I32, (dims.batch, dims.max_pages_per_seq)),
+            _buf(context_lens, "context_lens", _I32, (dims.batch,)))
+    pout = _buf(out, "out", _BF16, qshape)
+    _on(None, context_lens=context_lens, q=q, k_cache=k_cache, v_cache=v_cache,
+        block_table=block_table, kv_scales=kv_scales, out=out)
+    c = pa_plan_t()
+    _check(lib().pa_decode_static(ctypes.byref(dims), *ptrs, q_len, scale, kv_scale_mode, sc,
+                                  pout, ctypes.byref(c), _stream(stream)))
+    return Plan(c, None)
+
+
+def pa_static_scratch_bytes() -> int:
+    return int(lib().pa_static_scratch_bytes())
 
 
 def pa_plan_status(plan: Plan, stream=None) -> int:

@@ -51,6 +51,15 @@ constexpr int kMaxDevices = 64;
 std::mutex g_dev_mu;
 int g_cu_cache[kMaxDevices] = {0};
 
+// Workspace of pa_decode_static, for callers that cannot allocate device
+// memory: one array per device, held until the process ends. Host code never
+// uses the array's name as an address (on the host it is a stand-in); it
+// uses the device address hipGetSymbolAddress returns, looked up once per
+// device with that device current.
+constexpr uint64_t kStaticScratchBytes = uint64_t(32) << 20;
+__device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+void* g_scratch_ptr[kMaxDevices] = {nullptr};
+
 // Validates dims and applies defaults into *out. Host-only. need_decode:
 // the rows per kv head must fit a decode instantiation (not for the append,
 // which takes any q_len).
@@ -546,6 +555,50 @@ int pa_cache_append(const pa_dims* dims, const void* new_k, const void* new_v,
                                      static_cast<hipStream_t>(stream)),
                    "append launch") ?: ok();
 }
+
+int pa_decode_static(const pa_dims* dims, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_table, const int32_t* context_lens, int32_t q_len,
+                     float scale, int32_t kv_scale_mode, const float* kv_scales, void* out,
+                     pa_plan_t* plan_out, void* stream) {
+  pa_dims d;
+  int v = -1, qb = 0;
+  if (int rc = check_dims(dims, &d, &v, true, &qb)) return rc;
+  int dev = -1;
+  if (int rc = current_device(&dev)) return rc;
+  int32_t cus = 0;
+  if (int rc = pa_query_device(dev, &cus)) return rc;
+  const uint64_t need = geometry(d, cus, qb).total;
+  if (need > kStaticScratchBytes)
+    return fail(PA_ERR_WORKSPACE,
+                "pa_decode_static: this problem needs %llu bytes of workspace; the static scratch "
+                "holds %llu (use pa_plan with a caller workspace)",
+                static_cast<unsigned long long>(need),
+                static_cast<unsigned long long>(kStaticScratchBytes));
+  void* ws = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    if (!g_scratch_ptr[dev]) {
+      void* p = nullptr;
+      const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !p)
+        return fail(PA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                    hipGetErrorString(e));
+      g_scratch_ptr[dev] = p;
+    }
+    ws = g_scratch_ptr[dev];
+  }
+  // the plan kernel writes every table and status word the decode reads, so
+  // nothing left in the scratch by an earlier call needs clearing
+  pa_plan_t plan;
+  if (int rc = pa_plan(dims, context_lens, ws, kStaticScratchBytes, &plan, stream)) return rc;
+  if (int rc = pa_decode(&plan, q, k_cache, v_cache, block_table, context_lens, q_len, scale,
+                         kv_scale_mode, kv_scales, out, stream))
+    return rc;
+  if (plan_out) *plan_out = plan;
+  return ok();
+}
+
+uint64_t pa_static_scratch_bytes(void) { return kStaticScratchBytes; }
 
 const char* pa_status_string(int status) {
   switch (status) {
