@@ -136,6 +136,14 @@ def parse():
     p.add_argument("--plan-sweep", action="store_true",
                    help="instead of the step bench: time pa_plan alone over batch sizes from "
                         "64 x 8 to 16384 x 8 (sequences x kv heads)")
+    p.add_argument("--tune", action="store_true",
+                   help="instead of the step bench: time every (grid multiplier, partition size, "
+                        "fused or separate reduce) per workload and write the tuning table")
+    p.add_argument("--tune-out", default="",
+                   help="where --tune writes the table (default: the package's tuning.csv)")
+    p.add_argument("--tune-margin", type=float, default=0.02,
+                   help="a setting other than the default must be faster by this fraction, "
+                        "in graph replays and in eager launches alike")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run one 512 MiB device copy first (a known-size kernel for scaling "
                         "rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -144,6 +152,23 @@ def parse():
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# workloads whose configuration states the partition size (split-KV
+# partitions of 256 tokens); the others leave it to the library (its tuning
+# table, else 256)
+PARTITION_STATED = ("C2_single_seq", "C4_fp8_q1_per_token", "C4_fp8_q4_per_token",
+                    "C4_fp8_q1_per_tensor", "C4_fp8_q4_per_tensor")
+
+
+def partition_of(name, spec):
+    return spec.partition_size if name in PARTITION_STATED else 0
+
+
+def tuned_entry(name, dims, cus):
+    """The tuning-table row pa_plan applies to these dims, if any."""
+    from paged_attention_decode_block_amd import tuning
+    return tuning.lookup(tuning.read_table(), tuning.shape_key(dims, cus))
 
 
 def main():
@@ -177,6 +202,9 @@ def main():
     if args.plan_sweep:
         plan_sweep(args, flush)
         return
+    if args.tune:
+        tune(args, flush)
+        return
     if args.calibrate_copy:
         src = torch.ones(1 << 27, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -203,7 +231,7 @@ def main():
                             page_size=spec.page_size, num_pages=w.num_pages,
                             max_pages_per_seq=spec.max_pages_per_seq, kv_dtype=kvd,
                             kv_scale_mode=mode,
-                            partition_size=args.partition or spec.partition_size,
+                            partition_size=args.partition or partition_of(name, spec),
                             grid_multiplier=args.grid_multiplier)
         ws = torch.empty(pa.pa_workspace_bytes(dims, cus), dtype=torch.uint8, device=dev)
         out = torch.empty_like(d["q"])
@@ -300,6 +328,11 @@ def main():
         r["decode_frac_of_peak"] = r["decode_GBps"] / HBM_PEAK_GBS
         r["variant"] = int(plan.c.variant)
         r["grid"] = int(plan.c.grid)
+        r["chosen"] = {"grid_multiplier": int(plan.c.dims.grid_multiplier),
+                       "partition_size": int(plan.c.dims.partition_size),
+                       "reduce": "fused" if plan.c.dims.flags & pa.PA_FLAG_FUSED_REDUCE
+                       else "separate",
+                       "source": "tuning table" if tuned_entry(name, dims, cus) else "default"}
         results[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
         log(f"{name}: step {r['step_us']:.1f}us (plan {r['plan_us']:.1f}, partition "
             f"{r['partition_us']:.1f}, reduce {r['reduce_us']:.1f}) -> {r['step_GBps']:.0f} GB/s "
@@ -587,6 +620,119 @@ def plan_sweep(args, flush):
         del ws, ctx
     print(json.dumps({"metric": "pa_plan time vs batch size", "unit": "us", "steps": args.steps,
                       "warmup": args.warmup, "points": points}), flush=True)
+
+
+def tune(args, flush):
+    """The offline tuner of the persistent grid ("[Kernel][Perf] Optimize
+    paged-attention metadata decode", ROCm/FlyDSL PR #910, "Pull request
+    overview": a tuned per-shape grid table written by a graph-based tuner).
+    Per workload, pa_decode (plan built beforehand) runs with every candidate
+    (grid multiplier, partition size, fused or separate reduce), captured once
+    in a HIP graph and replayed after a read flush, and launched eagerly the
+    same way; medians of HIP-event samples. The fastest candidate by graph
+    replay enters the table for the workload's shape class if it beats the
+    default (one workgroup per CU, 256 tokens, separate reduce) by the margin
+    in both timings; otherwise the default is recorded. Partition sizes vary
+    only where the workload's configuration leaves them open. Prints one JSON
+    line and writes the table."""
+    import torch
+
+    import paged_attention_decode_block_amd as pa
+    import workloads as W
+    from paged_attention_decode_block_amd import tuning
+
+    dev = torch.device("cuda:0")
+    cus = pa.pa_query_device(0)
+    stream = torch.cuda.current_stream()
+    out_path = args.tune_out or tuning.TABLE
+    table = tuning.read_table(out_path) if os.path.exists(out_path) else []
+    names = [n for n in W.CONFIGS] if not args.only else args.only.split(",")
+    report = {}
+    default = (1, 256, 0)
+    for name in names:
+        spec = W.CONFIGS[name]
+        w = W.generate(spec, args.seed)
+        d = {k: getattr(w, k).to(dev) for k in ("q", "k_cache", "v_cache", "block_table",
+                                                 "context_lens")}
+        kvs = None if w.kv_scales is None else w.kv_scales.to(dev)
+        mode = {W.SCALE_NONE: pa.PA_SCALE_NONE, W.SCALE_PER_TENSOR: pa.PA_SCALE_PER_TENSOR,
+                W.SCALE_PER_TOKEN_HEAD: pa.PA_SCALE_PER_TOKEN_HEAD}[spec.kv_scale_mode]
+        kvd = pa.PA_KV_FP8_E4M3FN if spec.kv_dtype == W.KV_FP8 else pa.PA_KV_BF16
+        partitions = (256,) if name in PARTITION_STATED else (128, 256, 512)
+        out = torch.empty_like(d["q"])
+        times = {}
+        key = None
+        for mult in (1, 2):
+            for P in partitions:
+                for fused in (0, 1):
+                    dims = pa.make_dims(batch=spec.batch, q_len=spec.q_len,
+                                        num_q_heads=spec.num_q_heads,
+                                        num_kv_heads=spec.num_kv_heads, head_dim=spec.head_dim,
+                                        page_size=spec.page_size, num_pages=w.num_pages,
+                                        max_pages_per_seq=spec.max_pages_per_seq, kv_dtype=kvd,
+                                        kv_scale_mode=mode, partition_size=P,
+                                        grid_multiplier=mult,
+                                        flags=pa.PA_FLAG_FUSED_REDUCE if fused
+                                        else pa.PA_FLAG_SEPARATE_REDUCE)
+                    key = tuning.shape_key(dims, cus)
+                    ws = torch.empty(pa.pa_workspace_bytes(dims, cus), dtype=torch.uint8,
+                                     device=dev)
+                    plan = pa.pa_plan(dims, d["context_lens"], workspace=ws, stream=stream)
+
+                    def call():
+                        pa.pa_decode(plan, d["q"], d["k_cache"], d["v_cache"], d["block_table"],
+                                     d["context_lens"], spec.q_len, spec.scale, mode, kvs, out,
+                                     stream=torch.cuda.current_stream())
+
+                    call()
+                    torch.cuda.synchronize()
+                    side = torch.cuda.Stream()
+                    side.wait_stream(torch.cuda.current_stream())
+                    graph = torch.cuda.CUDAGraph()
+                    with torch.cuda.stream(side):
+                        with torch.cuda.graph(graph, stream=side):
+                            call()
+                    torch.cuda.current_stream().wait_stream(side)
+                    res = {}
+                    for label, body in (("graph", graph.replay), ("eager", call)):
+                        ts = []
+                        for i in range(args.warmup + args.steps):
+                            if flush is not None:
+                                flush()
+                            e0 = torch.cuda.Event(enable_timing=True)
+                            e1 = torch.cuda.Event(enable_timing=True)
+                            e0.record()
+                            body()
+                            e1.record()
+                            e1.synchronize()
+                            if i >= args.warmup:
+                                ts.append(e0.elapsed_time(e1) * 1e3)
+                        res[label] = statistics.median(ts)
+                    assert pa.pa_plan_status(plan) == 0, f"tune {name} {(mult, P, fused)}"
+                    times[(mult, P, fused)] = res
+                    log(f"tune {name} mult={mult} P={P} fused={fused}: graph "
+                        f"{res['graph']:.1f} us, eager {res['eager']:.1f} us")
+                    del graph, ws, plan
+        best = min(times, key=lambda c: times[c]["graph"])
+        base = times[default]
+        m = 1 - args.tune_margin
+        if best != default and not (times[best]["graph"] < m * base["graph"]
+                                    and times[best]["eager"] < m * base["eager"]):
+            best = default
+        e = tuning.Entry(*key, grid_multiplier=best[0], partition_size=best[1],
+                         fused_reduce=best[2], decode_us=round(times[best]["eager"], 2),
+                         workload=name)
+        table = tuning.upsert(table, e)
+        report[name] = {"key": list(key), "chosen": list(best),
+                        "times_us": {f"m{c[0]}_p{c[1]}_{'fused' if c[2] else 'separate'}": v
+                                     for c, v in times.items()}}
+        log(f"tune {name}: chose mult={best[0]} P={best[1]} fused={best[2]}")
+        del d, kvs, out, w
+        torch.cuda.empty_cache()
+    tuning.write_table(table, out_path)
+    print(json.dumps({"metric": "pa_decode time per tuning candidate", "unit": "us",
+                      "steps": args.steps, "warmup": args.warmup, "margin": args.tune_margin,
+                      "table": out_path, "workloads": report}), flush=True)
 
 
 def decode_loop_bench(args):

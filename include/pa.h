@@ -94,10 +94,25 @@ enum {
 
 enum { PA_KV_BF16 = 0, PA_KV_FP8_E4M3FN = 1 };
 enum { PA_SCALE_NONE = 0, PA_SCALE_PER_TENSOR = 1, PA_SCALE_PER_TOKEN_HEAD = 2 };
-enum { PA_FLAG_DEBUG_BOUNDS = 1 };
+enum {
+  PA_FLAG_DEBUG_BOUNDS = 1,    /* check every block-table entry the decode reads */
+  PA_FLAG_FUSED_REDUCE = 2,    /* merge split pairs inside the partition pass: the
+                                  last workgroup of a pair to finish (a per-pair
+                                  arrival counter) merges its partials, in slot
+                                  order, with the reduce kernel's arithmetic;
+                                  the output is bitwise that of the separate
+                                  reduce ([P3] overview: split reduction)     */
+  PA_FLAG_SEPARATE_REDUCE = 4  /* merge them in a reduce kernel of its own.
+                                  With neither reduce flag, pa_plan takes the
+                                  tuned choice for the shape (pa_plan_choice),
+                                  else the separate reduce                   */
+};
 
-/* Problem description. Zero in partition_size / grid_multiplier selects the
- * default (256 tokens; one persistent workgroup per CU, [P3] "Summary"). */
+/* Problem description. Zero in partition_size / grid_multiplier, and neither
+ * reduce flag, select the tuned choice for the shape class when the library's
+ * tuning table has one (pa_plan_choice), else the defaults: 256 tokens, one
+ * persistent workgroup per CU ([P3] "Summary": the safe default) and the
+ * separate reduce. */
 typedef struct pa_dims {
   int32_t batch;
   int32_t q_len;               /* appended query tokens per sequence, >= 1.
@@ -116,8 +131,10 @@ typedef struct pa_dims {
   int32_t max_pages_per_seq;   /* block_table row stride                     */
   int32_t kv_dtype;            /* PA_KV_*                                    */
   int32_t kv_scale_mode;       /* PA_SCALE_*                                 */
-  int32_t partition_size;      /* tokens per work item, multiple of 16       */
-  int32_t grid_multiplier;     /* persistent workgroups per CU, 1..16        */
+  int32_t partition_size;      /* tokens per work item, multiple of 16; 0:
+                                  tuned or 256                               */
+  int32_t grid_multiplier;     /* persistent workgroups per CU, 1..16; 0:
+                                  tuned or 1                                 */
   int32_t flags;               /* PA_FLAG_*                                  */
 } pa_dims;
 
@@ -160,7 +177,8 @@ typedef struct pa_plan_t {
                                   its segment range end, then zeros          */
   uint64_t block_bytes;        /* workspace per block: block j's regions are
                                   at the offsets above plus j * block_bytes  */
-  uint64_t reserved;
+  uint64_t off_counters;       /* int32[num_pairs]: arrivals per split pair
+                                  (fused reduce), zeroed by pa_plan          */
 } pa_plan_t;
 
 #define PA_PLAN_MAGIC 0x50414450u
@@ -168,6 +186,19 @@ typedef struct pa_plan_t {
 /* Number of compute units of HIP device `device` (cached after the first
  * call). Errors: PA_ERR_NULL, PA_ERR_DEVICE. */
 int pa_query_device(int32_t device, int32_t* num_cus);
+
+/* The settings pa_plan would use for `dims` on a device with `num_cus` CUs:
+ * *chosen = dims with partition_size, grid_multiplier and the reduce flag
+ * filled in (exactly one of PA_FLAG_FUSED_REDUCE / PA_FLAG_SEPARATE_REDUCE
+ * set). Fields the caller set are kept. The rest come from the library's
+ * tuning table ([P3] overview: a tuned per-shape persistent grid, with a
+ * lookup that keeps the defaults when a shape has no entry), keyed by the
+ * shape class (num_cus, head_dim, kv_dtype, kv_scale_mode, ceil(rows / 16)
+ * with rows = q_len * num_q_heads / num_kv_heads, page_size,
+ * floor(log2(batch * num_kv_heads)), floor(log2(max_pages_per_seq *
+ * page_size))); with no entry, from the defaults (pa_dims). Host-only.
+ * Errors: as pa_workspace_bytes. */
+int pa_plan_choice(const pa_dims* dims, int32_t num_cus, pa_dims* chosen);
 
 /* Workspace bytes a plan for `dims` on a device with `num_cus` CUs needs.
  * Host-only; validates dims exactly as pa_plan does. Errors: PA_ERR_NULL,
@@ -221,6 +252,9 @@ int pa_plan(const pa_dims* dims, const int32_t* context_lens, void* workspace,
  * the work. A live length below the plan's, or past that capacity, sets
  * PA_DEV_BAD_CONTEXT, and that sequence is decoded over the plan's length.
  *
+ * A plan built with PA_FLAG_FUSED_REDUCE (or so tuned) launches the
+ * partition pass only; it merges the split pairs itself.
+ *
  * Errors: PA_ERR_NULL, PA_ERR_ALIGN, PA_ERR_PLAN_MISMATCH, PA_ERR_SCALE_MODE,
  * PA_ERR_HIP. */
 int pa_decode(const pa_plan_t* plan, const void* q, const void* k_cache, const void* v_cache,
@@ -233,7 +267,8 @@ int pa_decode(const pa_plan_t* plan, const void* q, const void* k_cache, const v
  * (merges the partials). pa_decode == pa_decode_partition then
  * pa_decode_reduce on the same stream; same arguments and errors. When
  * partition_size >= max_pages_per_seq * page_size no pair can be split, and
- * pa_decode_reduce validates its arguments and launches nothing. */
+ * pa_decode_reduce validates its arguments and launches nothing; likewise
+ * for a fused-reduce plan, whose partition pass merges the split pairs. */
 int pa_decode_partition(const pa_plan_t* plan, const void* q, const void* k_cache,
                         const void* v_cache, const int32_t* block_table,
                         const int32_t* context_lens, int32_t q_len, float scale,

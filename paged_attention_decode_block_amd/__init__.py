@@ -51,6 +51,8 @@ PA_SCALE_NONE = 0
 PA_SCALE_PER_TENSOR = 1
 PA_SCALE_PER_TOKEN_HEAD = 2
 PA_FLAG_DEBUG_BOUNDS = 1
+PA_FLAG_FUSED_REDUCE = 2
+PA_FLAG_SEPARATE_REDUCE = 4
 PA_PLAN_MAGIC = 0x50414450
 
 
@@ -82,7 +84,7 @@ class pa_plan_t(ctypes.Structure):
         ("off_batch_base", ctypes.c_uint64), ("off_partial_lse", ctypes.c_uint64),
         ("off_partial_o", ctypes.c_uint64), ("off_seg_info", ctypes.c_uint64),
         ("off_wg_head", ctypes.c_uint64), ("block_bytes", ctypes.c_uint64),
-        ("reserved", ctypes.c_uint64),
+        ("off_counters", ctypes.c_uint64),
     ]
 
 
@@ -102,6 +104,7 @@ def lib() -> ctypes.CDLL:
         sig = {
             "pa_query_device": (ctypes.c_int, [i32, P(i32)]),
             "pa_workspace_bytes": (ctypes.c_int, [P(pa_dims), i32, P(u64)]),
+            "pa_plan_choice": (ctypes.c_int, [P(pa_dims), i32, P(pa_dims)]),
             "pa_plan": (ctypes.c_int, [P(pa_dims), vp, vp, u64, P(pa_plan_t), vp]),
             "pa_decode": (ctypes.c_int, [P(pa_plan_t), vp, vp, vp, vp, vp, i32, ctypes.c_float,
                                          i32, vp, vp, vp]),
@@ -236,6 +239,15 @@ def pa_query_device(device: int = 0) -> int:
     n = ctypes.c_int32(0)
     _check(lib().pa_query_device(device, ctypes.byref(n)))
     return n.value
+
+
+def pa_plan_choice(dims: pa_dims, num_cus: int) -> pa_dims:
+    """The dims pa_plan would use on a device of num_cus CUs: partition size,
+    grid multiplier and reduce flag filled in from the tuning table or the
+    defaults (include/pa.h, pa_plan_choice)."""
+    out = pa_dims()
+    _check(lib().pa_plan_choice(ctypes.byref(dims), num_cus, ctypes.byref(out)))
+    return out
 
 
 def pa_workspace_bytes(dims: pa_dims, num_cus: int) -> int:

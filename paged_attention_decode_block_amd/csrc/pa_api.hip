@@ -51,6 +51,42 @@ constexpr int kMaxDevices = 64;
 std::mutex g_dev_mu;
 int g_cu_cache[kMaxDevices] = {0};
 
+// Tuned settings per shape class ([P3] overview: the persistent grid is
+// looked up per shape in a tuned table, with the one-grid-per-CU default
+// where a shape has none). The rows are generated at build time from the
+// committed CSV table (tuning.csv beside the package, written by
+// `bench.py --tune`); a row of -1 ends the list.
+struct TuneEntry {
+  int32_t num_cus, head_dim, kv_dtype, kv_scale_mode, row_tiles, page_size, pairs_log2,
+      capacity_log2;
+  int32_t grid_multiplier, partition_size, fused;
+};
+const TuneEntry kTuned[] = {
+#include "pa_tuning_table.inc"
+    {-1, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0}};
+
+int floor_log2(int64_t x) {
+  int r = -1;
+  while (x > 0) {
+    x >>= 1;
+    ++r;
+  }
+  return r;
+}
+
+const TuneEntry* tuned(const pa_dims& d, int num_cus) {
+  const int64_t rows = static_cast<int64_t>(d.q_len) * (d.num_q_heads / d.num_kv_heads);
+  const int rt = static_cast<int>(std::min<int64_t>((rows + 15) / 16, 1 << 20));
+  const int pl = floor_log2(static_cast<int64_t>(d.batch) * d.num_kv_heads);
+  const int cl = floor_log2(static_cast<int64_t>(d.max_pages_per_seq) * d.page_size);
+  for (const TuneEntry* e = kTuned; e->num_cus >= 0; ++e)
+    if (e->num_cus == num_cus && e->head_dim == d.head_dim && e->kv_dtype == d.kv_dtype &&
+        e->kv_scale_mode == d.kv_scale_mode && e->row_tiles == rt && e->page_size == d.page_size &&
+        e->pairs_log2 == pl && e->capacity_log2 == cl)
+      return e;
+  return nullptr;
+}
+
 // Workspace of pa_decode_static, for callers that cannot allocate device
 // memory: one array per device, held until the process ends. Host code never
 // uses the array's name as an address (on the host it is a stand-in); it
@@ -60,25 +96,39 @@ constexpr uint64_t kStaticScratchBytes = uint64_t(32) << 20;
 __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
 void* g_scratch_ptr[kMaxDevices] = {nullptr};
 
-// Validates dims and applies defaults into *out. Host-only. need_decode:
-// the rows per kv head must fit a decode instantiation (not for the append,
-// which takes any q_len).
+constexpr int kReduceFlags = PA_FLAG_FUSED_REDUCE | PA_FLAG_SEPARATE_REDUCE;
+
+// Validates dims and applies the tuned choice (num_cus > 0) and the defaults
+// into *out. Host-only. need_decode: the rows per kv head must fit a decode
+// instantiation (not for the append, which takes any q_len).
 int check_dims(const pa_dims* in, pa_dims* out, int* variant, bool need_decode = true,
-               int* q_block = nullptr) {
+               int* q_block = nullptr, int num_cus = 0) {
   if (!in) return fail(PA_ERR_NULL, "dims is NULL");
   pa_dims d = *in;
-  if (d.partition_size == 0) d.partition_size = kDefaultPartition;
-  if (d.grid_multiplier == 0) d.grid_multiplier = 1;
   if (d.batch < 1 || d.q_len < 1 || d.num_q_heads < 1 || d.num_kv_heads < 1 || d.num_pages < 1 ||
       d.max_pages_per_seq < 1)
     return fail(PA_ERR_DIMS, "batch, q_len, heads, num_pages and max_pages_per_seq must be >= 1");
   if (d.num_q_heads % d.num_kv_heads != 0)
     return fail(PA_ERR_DIMS, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)",
                 d.num_q_heads, d.num_kv_heads);
+  if (d.flags & ~(PA_FLAG_DEBUG_BOUNDS | kReduceFlags))
+    return fail(PA_ERR_DIMS, "unknown flag bits 0x%x", d.flags);
+  if ((d.flags & kReduceFlags) == kReduceFlags)
+    return fail(PA_ERR_DIMS, "PA_FLAG_FUSED_REDUCE and PA_FLAG_SEPARATE_REDUCE are exclusive");
+  if (num_cus > 0 && (d.partition_size == 0 || d.grid_multiplier == 0 || !(d.flags & kReduceFlags))) {
+    if (const TuneEntry* e = tuned(d, num_cus)) {
+      if (d.partition_size == 0) d.partition_size = e->partition_size;
+      if (d.grid_multiplier == 0) d.grid_multiplier = e->grid_multiplier;
+      if (!(d.flags & kReduceFlags))
+        d.flags |= e->fused ? PA_FLAG_FUSED_REDUCE : PA_FLAG_SEPARATE_REDUCE;
+    }
+  }
+  if (d.partition_size == 0) d.partition_size = kDefaultPartition;
+  if (d.grid_multiplier == 0) d.grid_multiplier = 1;
+  if (!(d.flags & kReduceFlags)) d.flags |= PA_FLAG_SEPARATE_REDUCE;
   if (d.grid_multiplier < 1 || d.grid_multiplier > kMaxGridMultiplier)
     return fail(PA_ERR_DIMS, "grid_multiplier %d outside [1, %d]", d.grid_multiplier,
                 kMaxGridMultiplier);
-  if (d.flags & ~PA_FLAG_DEBUG_BOUNDS) return fail(PA_ERR_DIMS, "unknown flag bits 0x%x", d.flags);
   if (d.head_dim != 128 && d.head_dim != 256)
     return fail(PA_ERR_UNSUPPORTED, "head_dim %d not supported (128 or 256)", d.head_dim);
   if (!pow2(d.page_size) || d.page_size < 16 || d.page_size > 1024)
@@ -130,7 +180,7 @@ int check_dims(const pa_dims* in, pa_dims* out, int* variant, bool need_decode =
 
 struct Layout {
   uint64_t status, wg_begin, wg_seg_begin, items, segs, nseg, seg_base, pseg_base, batch_base,
-      partial_lse, partial_o, seg_info, wg_head, total;
+      partial_lse, partial_o, seg_info, wg_head, counters, total;
   int32_t grid, pairs, rows, max_items, max_segs;
 };
 
@@ -163,6 +213,7 @@ Layout layout(const pa_dims& d, int num_cus) {
   L.partial_o = take(4ull * L.max_segs * L.rows * d.head_dim);
   L.seg_info = take(32ull * L.max_segs);
   L.wg_head = take(64ull * L.grid);
+  L.counters = take(4ull * L.pairs);
   L.total = off;
   return L;
 }
@@ -263,6 +314,7 @@ pa::DecodeArgs decode_args(const pa_plan_t* plan, const void* q, const void* k_c
   a.partial_o = at<float>(plan, plan->off_partial_o + wb);
   a.partial_lse = at<float>(plan, plan->off_partial_lse + wb);
   a.status = at<int32_t>(plan, plan->off_status + wb);
+  a.counters = (d.flags & PA_FLAG_FUSED_REDUCE) ? at<int32_t>(plan, plan->off_counters + wb) : nullptr;
   a.batch = d.batch;
   a.q_len = block_q_len(plan, blk);
   a.q_total = d.q_len;
@@ -321,12 +373,22 @@ int pa_query_device(int32_t device, int32_t* num_cus) {
   return ok();
 }
 
-int pa_workspace_bytes(const pa_dims* dims, int32_t num_cus, uint64_t* bytes) {
-  if (!bytes) return fail(PA_ERR_NULL, "bytes is NULL");
+int pa_plan_choice(const pa_dims* dims, int32_t num_cus, pa_dims* chosen) {
+  if (!chosen) return fail(PA_ERR_NULL, "chosen is NULL");
+  if (num_cus < 1 || num_cus > 65536) return fail(PA_ERR_DIMS, "num_cus %d out of range", num_cus);
   pa_dims d;
   int v = -1, qb = 0;
-  if (int rc = check_dims(dims, &d, &v, true, &qb)) return rc;
+  if (int rc = check_dims(dims, &d, &v, true, &qb, num_cus)) return rc;
+  *chosen = d;
+  return ok();
+}
+
+int pa_workspace_bytes(const pa_dims* dims, int32_t num_cus, uint64_t* bytes) {
+  if (!bytes) return fail(PA_ERR_NULL, "bytes is NULL");
   if (num_cus < 1 || num_cus > 65536) return fail(PA_ERR_DIMS, "num_cus %d out of range", num_cus);
+  pa_dims d;
+  int v = -1, qb = 0;
+  if (int rc = check_dims(dims, &d, &v, true, &qb, num_cus)) return rc;
   *bytes = geometry(d, num_cus, qb).total;
   return ok();
 }
@@ -335,6 +397,8 @@ int pa_plan(const pa_dims* dims, const int32_t* context_lens, void* workspace,
             uint64_t workspace_bytes, pa_plan_t* plan, void* stream) {
   pa_dims d;
   int v = -1, qb = 0;
+  // argument errors first, before any HIP call; the tuned choice needs the
+  // device's CU count, so the dims are checked again with it below
   if (int rc = check_dims(dims, &d, &v, true, &qb)) return rc;
   if (!context_lens || !plan) return fail(PA_ERR_NULL, "context_lens and plan are required");
   if (!workspace) return fail(PA_ERR_WORKSPACE, "workspace is NULL");
@@ -344,6 +408,7 @@ int pa_plan(const pa_dims* dims, const int32_t* context_lens, void* workspace,
   if (int rc = current_device(&dev)) return rc;
   int32_t cus = 0;
   if (int rc = pa_query_device(dev, &cus)) return rc;
+  if (int rc = check_dims(dims, &d, &v, true, &qb, cus)) return rc;
   const Geometry gm = geometry(d, cus, qb);
   const Layout& L = gm.L;
   if (workspace_bytes < gm.total)
@@ -379,6 +444,7 @@ int pa_plan(const pa_dims* dims, const int32_t* context_lens, void* workspace,
   p.off_partial_o = L.partial_o;
   p.off_seg_info = L.seg_info;
   p.off_wg_head = L.wg_head;
+  p.off_counters = L.counters;
 
   // one work list per block of queries; block j sees the keys up to its
   // last query, ctx - (q_len - its end) of them
@@ -398,6 +464,7 @@ int pa_plan(const pa_dims* dims, const int32_t* context_lens, void* workspace,
     a.batch_base = at<int32_t>(&p, p.off_batch_base + wb);
     a.seg_info = at<int32_t>(&p, p.off_seg_info + wb);
     a.wg_head = at<int32_t>(&p, p.off_wg_head + wb);
+    a.counters = at<int32_t>(&p, p.off_counters + wb);
     a.batch = d.batch;
     a.num_kv_heads = d.num_kv_heads;
     a.q_len = qj;
@@ -443,7 +510,8 @@ int pa_decode_reduce(const pa_plan_t* plan, int32_t q_len, int32_t kv_scale_mode
   // A context never longer than one partition (partition_size >= the block
   // table's capacity) makes every pair a single item, hence a single
   // segment, written out by the partition pass: nothing is left to merge.
-  if (plan->max_items <= plan->num_pairs) return ok();
+  // A fused-reduce plan's partition pass merged the split pairs itself.
+  if (plan->max_items <= plan->num_pairs || (plan->dims.flags & PA_FLAG_FUSED_REDUCE)) return ok();
   for (int j = 0; j < num_blocks(plan); ++j) {
     pa::DecodeArgs a = decode_args(plan, out, out, out, nullptr, nullptr, 1.0f, nullptr, out, j);
     if (int rc = hip_check(pa::launch_reduce(a, plan->dims.head_dim, plan->num_pairs,
@@ -567,6 +635,7 @@ int pa_decode_static(const pa_dims* dims, const void* q, const void* k_cache, co
   if (int rc = current_device(&dev)) return rc;
   int32_t cus = 0;
   if (int rc = pa_query_device(dev, &cus)) return rc;
+  if (int rc = check_dims(dims, &d, &v, true, &qb, cus)) return rc;
   const uint64_t need = geometry(d, cus, qb).total;
   if (need > kStaticScratchBytes)
     return fail(PA_ERR_WORKSPACE,

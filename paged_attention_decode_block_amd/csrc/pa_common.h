@@ -34,6 +34,7 @@ struct DecodeArgs {
   float* partial_o;             // [slots][rows][D]
   float* partial_lse;           // [slots][rows]
   int32_t* status;
+  int32_t* counters;            // [pairs] arrivals per split pair (fused reduce), or null
   int32_t batch, q_len, num_q_heads, num_kv_heads, group, rows;
   int32_t q_total;               // queries per sequence in q and out; q and out point at this
                                  // launch's block of q_len of them

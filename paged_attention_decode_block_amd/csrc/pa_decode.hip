@@ -82,6 +82,10 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
   return bf16x8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
+// s_waitcnt with vmcnt = 0 (gfx9 encoding; expcnt and lgkmcnt left at their
+// maxima): the wave's vector memory operations, stores included, are done.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 // Lane i of each lane quad's value, to every lane of the quad (DPP
 // quad_perm [i, i, i, i]).
 __device__ __forceinline__ float quad_bcast(float x, int i) {
@@ -438,7 +442,88 @@ __device__ __forceinline__ void load_q(const DecodeArgs& a, const Entry& e, int 
   }
 }
 
-template <int D, bool FP8, int SM, int RT, int NB, int NW, int NS, int RS, bool OPC, bool SH>
+// Log-sum-exp merge of one (row r, 8 dims from d0) unit of split pair (b, g),
+// whose n partials (O_s, lse_s) sit in slots base .. base + n - 1: M = max
+// lse_s, w_s = exp(lse_s - M), out = sum w_s O_s / sum w_s ("[Kernel][Perf]
+// Optimize paged-attention metadata decode", ROCm/FlyDSL PR #910, overview:
+// the split reduction kernel), read in slot order. It is latency-bound, so
+// the loads of 8 slots go out at once and fold in with a running maximum:
+// one round trip for pairs of up to 8 segments. The reduce kernel and the
+// fused reduce of the partition pass both call it, so the two give the same
+// bits.
+constexpr int kReduceBatch = 8;
+
+template <int D>
+__device__ __forceinline__ void reduce_unit(const DecodeArgs& a, int base, int n, int b, int g, int r,
+                                            int d0) {
+  const int R = a.rows;
+  const float* lse = a.partial_lse + static_cast<int64_t>(base) * R + r;
+  const float* po = a.partial_o + (static_cast<int64_t>(base) * R + r) * D + d0;
+  const int64_t so = static_cast<int64_t>(R) * D;  // slot stride in floats
+  float M = neg_inf(), W = 0.f;
+  f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+  for (int s0 = 0; s0 < n; s0 += kReduceBatch) {
+    float lv[kReduceBatch];
+    f32x4 x0[kReduceBatch], x1[kReduceBatch];
+#pragma unroll
+    for (int t = 0; t < kReduceBatch; ++t) {
+      lv[t] = neg_inf();
+      x0[t] = x1[t] = f32x4{0, 0, 0, 0};
+      if (s0 + t < n) {
+        lv[t] = lse[(s0 + t) * R];
+        x0[t] = *reinterpret_cast<const f32x4*>(po + (s0 + t) * so);
+        x1[t] = *reinterpret_cast<const f32x4*>(po + (s0 + t) * so + 4);
+      }
+    }
+    float mb = M;
+#pragma unroll
+    for (int t = 0; t < kReduceBatch; ++t) mb = fmaxf(mb, lv[t]);
+    if (mb == neg_inf()) continue;  // every slot so far is empty for this row
+    const float rescale = M == neg_inf() ? 0.f : __builtin_amdgcn_exp2f((M - mb) * kLog2e);
+    W *= rescale;
+    acc0 *= rescale;
+    acc1 *= rescale;
+    M = mb;
+#pragma unroll
+    for (int t = 0; t < kReduceBatch; ++t) {
+      const float wgt = __builtin_amdgcn_exp2f((lv[t] - M) * kLog2e);  // 0 for empty slots
+      W += wgt;
+      acc0 += wgt * x0[t];
+      acc1 += wgt * x1[t];
+    }
+  }
+  const float inv = W > 0.f ? 1.f / W : 0.f;
+  acc0 *= inv;
+  acc1 *= inv;
+  const int qi = r / a.group;
+  const int h = g * a.group + (r - qi * a.group);
+  const f32x8 f8 = {acc0.x, acc0.y, acc0.z, acc0.w, acc1.x, acc1.y, acc1.z, acc1.w};
+  *reinterpret_cast<bf16x8*>(a.out + ((static_cast<int64_t>(b) * a.q_total + qi) * a.num_q_heads + h) *
+                                         D + d0) = __builtin_convertvector(f8, bf16x8);
+}
+
+// Reduce kernel: one workgroup per (pair, block of 16 query rows); pairs with
+// a single segment were finished by the partition pass.
+constexpr int kReduceThreads = 256;
+constexpr int kReduceRows = 16;
+
+template <int D>
+__global__ __launch_bounds__(kReduceThreads) void reduce_kernel(DecodeArgs a) {
+  const int p = blockIdx.x;
+  const int n = ldu(a.nseg, p);
+  if (n <= 1) return;
+  const int base = ldu(a.seg_base, p);
+  const int b = p / a.num_kv_heads;
+  const int g = p - b * a.num_kv_heads;
+  constexpr int U = D / 8;  // 8-dim units per row
+  for (int u = threadIdx.x; u < kReduceRows * U; u += kReduceThreads) {
+    const int r = blockIdx.y * kReduceRows + u / U;
+    if (r < a.rows) reduce_unit<D>(a, base, n, b, g, r, (u % U) * 8);
+  }
+}
+
+template <int D, bool FP8, int SM, int RT, int NB, int NW, int NS, int RS, bool OPC, bool SH,
+          bool FUSED>
 __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(DecodeArgs a) {
   using C = Cfg<D, FP8, RT, NB, NW>;
   constexpr int KC = C::KC, DT = C::DT, TC = C::TC, LPB = C::LPB;
@@ -463,6 +548,7 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
   __shared__ __attribute__((aligned(16))) uint8_t lds_waves[SH ? NST * 2 * SHBUF : NW * C::WBYTES];
   __shared__ float st_m[NW][RT * 16];
   __shared__ float st_l[NW][RT * 16];
+  __shared__ int32_t s_last[2];  // fused reduce: this workgroup arrived last at pend[0] / pend[1]
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -838,77 +924,57 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
       if (!ev[0].live()) break;
     }
   }
-}
 
-// Log-sum-exp reduce: one workgroup per (pair, block of 16 query rows);
-// pairs with a single segment were finished by the partition pass. For row r
-// of a split pair with partials (O_s, lse_s): M = max lse_s,
-// w_s = exp(lse_s - M), out = sum w_s O_s / sum w_s ("[Kernel][Perf] Optimize
-// paged-attention metadata decode", ROCm/FlyDSL PR #910, overview: the split
-// reduction kernel). The kernel is latency-bound, so each thread (one row, 8
-// dims) issues the loads of 8 slots at once and folds them in with a running
-// maximum: one round trip for pairs of up to 8 segments.
-constexpr int kReduceThreads = 256;
-constexpr int kReduceRows = 16;
-constexpr int kReduceBatch = 8;
-
-template <int D>
-__global__ __launch_bounds__(kReduceThreads) void reduce_kernel(DecodeArgs a) {
-  const int p = blockIdx.x;
-  const int n = ldu(a.nseg, p);
-  if (n <= 1) return;
-  const int base = ldu(a.seg_base, p);
-  const int b = p / a.num_kv_heads;
-  const int g = p - b * a.num_kv_heads;
-  const int R = a.rows;
-  constexpr int U = D / 8;  // 8-dim units per row
-  for (int u = threadIdx.x; u < kReduceRows * U; u += kReduceThreads) {
-    const int r = blockIdx.y * kReduceRows + u / U;
-    const int d0 = (u % U) * 8;
-    if (r >= R) continue;
-    const float* lse = a.partial_lse + static_cast<int64_t>(base) * R + r;
-    const float* po = a.partial_o + (static_cast<int64_t>(base) * R + r) * D + d0;
-    const int64_t so = static_cast<int64_t>(R) * D;  // slot stride in floats
-    float M = neg_inf(), W = 0.f;
-    f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
-    for (int s0 = 0; s0 < n; s0 += kReduceBatch) {
-      float lv[kReduceBatch];
-      f32x4 x0[kReduceBatch], x1[kReduceBatch];
-#pragma unroll
-      for (int t = 0; t < kReduceBatch; ++t) {
-        lv[t] = neg_inf();
-        x0[t] = x1[t] = f32x4{0, 0, 0, 0};
-        if (s0 + t < n) {
-          lv[t] = lse[(s0 + t) * R];
-          x0[t] = *reinterpret_cast<const f32x4*>(po + (s0 + t) * so);
-          x1[t] = *reinterpret_cast<const f32x4*>(po + (s0 + t) * so + 4);
-        }
-      }
-      float mb = M;
-#pragma unroll
-      for (int t = 0; t < kReduceBatch; ++t) mb = fmaxf(mb, lv[t]);
-      if (mb == neg_inf()) continue;  // every slot so far is empty for this row
-      const float rescale = M == neg_inf() ? 0.f : __builtin_amdgcn_exp2f((M - mb) * kLog2e);
-      W *= rescale;
-      acc0 *= rescale;
-      acc1 *= rescale;
-      M = mb;
-#pragma unroll
-      for (int t = 0; t < kReduceBatch; ++t) {
-        const float wgt = __builtin_amdgcn_exp2f((lv[t] - M) * kLog2e);  // 0 for empty slots
-        W += wgt;
-        acc0 += wgt * x0[t];
-        acc1 += wgt * x1[t];
-      }
+  // Fused reduce (PA_FLAG_FUSED_REDUCE, the FUSED instantiations): once the
+  // workgroup's loads are over,
+  // it counts its arrival at each split pair it wrote a partial of; the
+  // workgroup that arrives last at a pair merges the pair's partials with the
+  // reduce kernel's arithmetic, in slot order, and clears the pair's counter
+  // for the next decode on the same plan. Release: every wave waits for its
+  // own stores, then wave 0 writes the XCD's L2 back (the agent-scope release
+  // fence) before its device-scope vector atomic add; acquire: the merging
+  // workgroup invalidates its caches (agent-scope acquire fence) before it
+  // reads the other workgroups' partials. The waits would drain the K/V loads
+  // in flight, so they sit here, after the last of them.
+  if constexpr (FUSED) {
+    // the split pairs this workgroup wrote partials of: only a range's first
+    // and last segments can belong to split pairs (a segment between them
+    // holds a whole pair), and the plan has both records
+    const i32x8 h0 = ldu(reinterpret_cast<const i32x8*>(a.wg_head), 2 * w);
+    const i32x8 h1 = ldu(reinterpret_cast<const i32x8*>(a.wg_head), 2 * w + 1);
+    const i32x8 rl = ldu(reinterpret_cast<const i32x8*>(a.seg_info), h1[0] - 1);
+    int32_t npend = 0, pend0 = -1, pend1 = -1;
+    if (h0[5] >= 0) pend0 = h0[7], npend = 1;                  // first segment: slot, pair
+    if (h1[0] - 1 > h0[0] && rl[4] >= 0) {                     // a last segment of its own
+      if (npend == 0) pend0 = rl[6]; else pend1 = rl[6];
+      ++npend;
     }
-    const float inv = W > 0.f ? 1.f / W : 0.f;
-    acc0 *= inv;
-    acc1 *= inv;
-    const int qi = r / a.group;
-    const int h = g * a.group + (r - qi * a.group);
-    const f32x8 f8 = {acc0.x, acc0.y, acc0.z, acc0.w, acc1.x, acc1.y, acc1.z, acc1.w};
-    *reinterpret_cast<bf16x8*>(a.out + ((static_cast<int64_t>(b) * a.q_total + qi) * a.num_q_heads + h) *
-                                           D + d0) = __builtin_convertvector(f8, bf16x8);
+    if (npend == 0) return;
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    if (wave == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      if (lane < npend) {
+        const int32_t pair = lane == 0 ? pend0 : pend1;
+        const int32_t before = __hip_atomic_fetch_add(a.counters + pair, 1, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT);
+        s_last[lane] = before == ldu(a.nseg, pair) - 1 ? 1 : 0;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    __syncthreads();
+    for (int k = 0; k < npend; ++k) {
+      if (!s_last[k]) continue;
+      const int32_t pair = k == 0 ? pend0 : pend1;
+      const int b = pair / a.num_kv_heads;
+      const int g = pair - b * a.num_kv_heads;
+      const int n = ldu(a.nseg, pair);
+      const int base = ldu(a.seg_base, pair);
+      constexpr int U = D / 8;
+      for (int u = threadIdx.x; u < a.rows * U; u += C::THREADS)
+        reduce_unit<D>(a, base, n, b, g, u / U, (u % U) * 8);
+      if (threadIdx.x == 0) a.counters[pair] = 0;
+    }
   }
 }
 
@@ -1009,7 +1075,14 @@ hipError_t launch_loader_t(const DecodeArgs& a, int max_segs, uint8_t* k_out, ui
 
 template <int D, bool FP8, int SM, int RT, int NB, int NW, int NS, int RS, bool OPC, bool SH>
 hipError_t launch_partition_t(const DecodeArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((partition_kernel<D, FP8, SM, RT, NB, NW, NS, RS, OPC, SH>), dim3(grid), dim3(NW * 64), 0, s, a);
+  // the fused reduce is an instantiation of its own, so the separate-reduce
+  // kernels carry none of its code
+  if (a.counters != nullptr)
+    hipLaunchKernelGGL((partition_kernel<D, FP8, SM, RT, NB, NW, NS, RS, OPC, SH, true>), dim3(grid),
+                       dim3(NW * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((partition_kernel<D, FP8, SM, RT, NB, NW, NS, RS, OPC, SH, false>), dim3(grid),
+                       dim3(NW * 64), 0, s, a);
   return hipGetLastError();
 }
 

@@ -19,6 +19,7 @@ struct PlanArgs {
   int32_t* batch_base;
   int32_t* seg_info;  // [max_segs][8] (b, g, tok_begin, tok_end, slot, ctx, pair, 0)
   int32_t* wg_head;   // [grid][16] (segment begin, first seg_info record, segment end, 0...)
+  int32_t* counters;  // [pairs] arrival counters of the fused reduce, zeroed by the plan
   int32_t batch, num_kv_heads, q_len, partition, grid;
   int32_t capacity;  // max_pages_per_seq * page_size
   // A block of q_len queries out of q_check per sequence: context lengths

@@ -209,7 +209,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   if (bad) {
     for (int i = gtid; i <= G; i += gstride) { a.wg_begin[i] = 0; a.wg_seg_begin[i] = 0; }
     for (int i = gtid; i < 16 * G; i += gstride) a.wg_head[i] = 0;
-    for (int i = gtid; i < pairs; i += gstride) a.nseg[i] = 0;
+    for (int i = gtid; i < pairs; i += gstride) {
+      a.nseg[i] = 0;
+      a.counters[i] = 0;
+    }
     for (int i = gtid; i <= pairs; i += gstride) { a.seg_base[i] = 0; a.pseg_base[i] = 0; }
     for (int i = gtid; i <= B; i += gstride) a.batch_base[i] = 0;
     if (gtid == 0) {
@@ -332,7 +335,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
           make_int4(first_seg, 0, 0, 0);
   }
 
-  // 5. tables the decode and the tests read, copied out of LDS
+  // 5. the fused reduce's arrival counters, cleared; the tables the decode
+  //    and the tests read, copied out of LDS
+  for (int32_t p = gtid; p < pairs; p += gstride) a.counters[p] = 0;
   if constexpr (kLds) {
     for (int32_t b = gtid; b <= B; b += gstride) a.batch_base[b] = t.base[b];
     for (int32_t p = gtid; p < pairs; p += gstride) {

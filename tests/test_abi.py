@@ -46,7 +46,8 @@ def _dims(**kw):
     (dict(num_q_heads=12, num_kv_heads=8), pa.PA_ERR_DIMS),
     (dict(num_pages=0), pa.PA_ERR_DIMS),
     (dict(grid_multiplier=17), pa.PA_ERR_DIMS),
-    (dict(flags=4), pa.PA_ERR_DIMS),
+    (dict(flags=8), pa.PA_ERR_DIMS),
+    (dict(flags=pa.PA_FLAG_FUSED_REDUCE | pa.PA_FLAG_SEPARATE_REDUCE), pa.PA_ERR_DIMS),
     (dict(head_dim=64), pa.PA_ERR_UNSUPPORTED),
     (dict(head_dim=96), pa.PA_ERR_UNSUPPORTED),
     (dict(page_size=8), pa.PA_ERR_UNSUPPORTED),
