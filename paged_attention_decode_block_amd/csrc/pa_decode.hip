@@ -86,6 +86,11 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
 // maxima): the wave's vector memory operations, stores included, are done.
 constexpr int kWaitVmcnt0 = 0x0F70;
 
+// Cache policy of a buffer access at agent scope (gfx950 sc1): a store is
+// written through to where every XCD sees it, a load does not hit a stale L2
+// line. The fused reduce's partials move between workgroups this way.
+constexpr int kSc1 = 16;
+
 // Lane i of each lane quad's value, to every lane of the quad (DPP
 // quad_perm [i, i, i, i]).
 __device__ __forceinline__ float quad_bcast(float x, int i) {
@@ -453,13 +458,20 @@ __device__ __forceinline__ void load_q(const DecodeArgs& a, const Entry& e, int 
 // bits.
 constexpr int kReduceBatch = 8;
 
-template <int D>
+// COH: the partials were written by other workgroups of the same launch, so
+// they are read with agent-scope coherent loads (sc1: past any stale L2 line).
+template <int D, bool COH = false>
 __device__ __forceinline__ void reduce_unit(const DecodeArgs& a, int base, int n, int b, int g, int r,
                                             int d0) {
   const int R = a.rows;
   const float* lse = a.partial_lse + static_cast<int64_t>(base) * R + r;
   const float* po = a.partial_o + (static_cast<int64_t>(base) * R + r) * D + d0;
   const int64_t so = static_cast<int64_t>(R) * D;  // slot stride in floats
+  // COH: resources over the pair's n slots
+  const rsrc_t rl = make_rsrc(a.partial_lse + static_cast<int64_t>(base) * R,
+                              static_cast<uint32_t>(n * R * 4));
+  const rsrc_t ro = make_rsrc(a.partial_o + static_cast<int64_t>(base) * R * D,
+                              static_cast<uint32_t>(n * R * D * 4));
   float M = neg_inf(), W = 0.f;
   f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
   for (int s0 = 0; s0 < n; s0 += kReduceBatch) {
@@ -470,9 +482,17 @@ __device__ __forceinline__ void reduce_unit(const DecodeArgs& a, int base, int n
       lv[t] = neg_inf();
       x0[t] = x1[t] = f32x4{0, 0, 0, 0};
       if (s0 + t < n) {
-        lv[t] = lse[(s0 + t) * R];
-        x0[t] = *reinterpret_cast<const f32x4*>(po + (s0 + t) * so);
-        x1[t] = *reinterpret_cast<const f32x4*>(po + (s0 + t) * so + 4);
+        if constexpr (COH) {
+          const uint32_t oo = static_cast<uint32_t>(((s0 + t) * R + r) * D + d0) * 4u;
+          lv[t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                rl, static_cast<uint32_t>((s0 + t) * R + r) * 4u, 0, kSc1));
+          x0[t] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, oo, 0, kSc1));
+          x1[t] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, oo + 16, 0, kSc1));
+        } else {
+          lv[t] = lse[(s0 + t) * R];
+          x0[t] = *reinterpret_cast<const f32x4*>(po + (s0 + t) * so);
+          x1[t] = *reinterpret_cast<const f32x4*>(po + (s0 + t) * so + 4);
+        }
       }
     }
     float mb = M;
@@ -559,6 +579,10 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
 
   // the workgroup's header: segment range and first segment, one load
   Cursor cur;
+  // FUSED: the split pairs this workgroup writes partials of (-1: none). Only
+  // a range's first and last segments can belong to split pairs (a segment
+  // between them holds a whole pair), and the plan has both records.
+  int32_t pend0 = -1, pend1 = -1;
   {
     const i32x8 h0 = ldu(reinterpret_cast<const i32x8*>(a.wg_head), 2 * w);
     const i32x8 h1 = ldu(reinterpret_cast<const i32x8*>(a.wg_head), 2 * w + 1);
@@ -567,6 +591,13 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
     if (cur.s >= cur.s_end) return;
     cur.live = 1;
     const i32x8 r = {h0[1], h0[2], h0[3], h0[4], h0[5], h0[6], h0[7], 0};
+    if constexpr (FUSED) {
+      const i32x8 rl = ldu(reinterpret_cast<const i32x8*>(a.seg_info), cur.s_end - 1);
+      if (r[4] >= 0) pend0 = r[6];                            // first segment: slot, pair
+      if (cur.s_end - 1 > cur.s && rl[4] >= 0) {               // a last segment of its own
+        if (pend0 < 0) pend0 = rl[6]; else pend1 = rl[6];
+      }
+    }
     cursor_set(cur, r, stream, a);
   }
 
@@ -894,6 +925,20 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
               const bf16x8 ob8 = __builtin_convertvector(f8, bf16x8);
               *reinterpret_cast<bf16x8*>(a.out + ((static_cast<int64_t>(e0.b) * a.q_total + qi) *
                                                       a.num_q_heads + h) * D + d0) = ob8;
+            } else if constexpr (FUSED) {
+              // agent-scope stores: the pair's last workgroup reads them
+              const rsrc_t ro = make_rsrc(a.partial_o + static_cast<int64_t>(e0.slot) * pair_rows * D,
+                                          static_cast<uint32_t>(pair_rows * D * 4));
+              const uint32_t oo = static_cast<uint32_t>(r * D + d0) * 4u;
+              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc0), ro, oo, 0, kSc1);
+              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc1), ro, oo + 16, 0, kSc1);
+              if (d0 == 0) {
+                const rsrc_t rl = make_rsrc(a.partial_lse + static_cast<int64_t>(e0.slot) * pair_rows,
+                                            static_cast<uint32_t>(pair_rows * 4));
+                const float lse = L > 0.f ? (Mru + __log2f(L)) * kLn2 : neg_inf();
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int32_t, lse), rl,
+                                                      static_cast<uint32_t>(r) * 4u, 0, kSc1);
+              }
             } else {
               float* dst = a.partial_o + (static_cast<int64_t>(e0.slot) * pair_rows + r) * D + d0;
               *reinterpret_cast<f32x4*>(dst) = acc0;
@@ -925,54 +970,40 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
     }
   }
 
-  // Fused reduce (PA_FLAG_FUSED_REDUCE, the FUSED instantiations): once the
-  // workgroup's loads are over,
-  // it counts its arrival at each split pair it wrote a partial of; the
-  // workgroup that arrives last at a pair merges the pair's partials with the
-  // reduce kernel's arithmetic, in slot order, and clears the pair's counter
-  // for the next decode on the same plan. Release: every wave waits for its
-  // own stores, then wave 0 writes the XCD's L2 back (the agent-scope release
-  // fence) before its device-scope vector atomic add; acquire: the merging
-  // workgroup invalidates its caches (agent-scope acquire fence) before it
-  // reads the other workgroups' partials. The waits would drain the K/V loads
-  // in flight, so they sit here, after the last of them.
+  // Fused reduce (PA_FLAG_FUSED_REDUCE, the FUSED instantiations). The
+  // workgroup wrote its split pairs' partials with agent-scope stores (sc1:
+  // written through to where every XCD sees them). Once its loads are over,
+  // every wave waits for its stores; then wave 0 counts the workgroup's
+  // arrival at each such pair with a device-scope vector atomic add. The
+  // workgroup that arrives last at a pair merges the pair's partials, read
+  // with agent-scope loads (sc1: never a stale L2 line), with the reduce
+  // kernel's arithmetic in slot order, and clears the pair's counter for the
+  // next decode on the same plan. No cache-wide write-back or invalidation is
+  // needed, and the waits sit after the last K/V loads.
   if constexpr (FUSED) {
-    // the split pairs this workgroup wrote partials of: only a range's first
-    // and last segments can belong to split pairs (a segment between them
-    // holds a whole pair), and the plan has both records
-    const i32x8 h0 = ldu(reinterpret_cast<const i32x8*>(a.wg_head), 2 * w);
-    const i32x8 h1 = ldu(reinterpret_cast<const i32x8*>(a.wg_head), 2 * w + 1);
-    const i32x8 rl = ldu(reinterpret_cast<const i32x8*>(a.seg_info), h1[0] - 1);
-    int32_t npend = 0, pend0 = -1, pend1 = -1;
-    if (h0[5] >= 0) pend0 = h0[7], npend = 1;                  // first segment: slot, pair
-    if (h1[0] - 1 > h0[0] && rl[4] >= 0) {                     // a last segment of its own
-      if (npend == 0) pend0 = rl[6]; else pend1 = rl[6];
-      ++npend;
-    }
-    if (npend == 0) return;
+    if (pend0 < 0) return;
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     if (wave == 0) {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      const int npend = pend1 >= 0 ? 2 : 1;
       if (lane < npend) {
         const int32_t pair = lane == 0 ? pend0 : pend1;
         const int32_t before = __hip_atomic_fetch_add(a.counters + pair, 1, __ATOMIC_RELAXED,
                                                       __HIP_MEMORY_SCOPE_AGENT);
         s_last[lane] = before == ldu(a.nseg, pair) - 1 ? 1 : 0;
       }
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
     __syncthreads();
-    for (int k = 0; k < npend; ++k) {
-      if (!s_last[k]) continue;
+    for (int k = 0; k < 2; ++k) {
       const int32_t pair = k == 0 ? pend0 : pend1;
+      if (pair < 0 || !s_last[k]) continue;
       const int b = pair / a.num_kv_heads;
       const int g = pair - b * a.num_kv_heads;
       const int n = ldu(a.nseg, pair);
       const int base = ldu(a.seg_base, pair);
       constexpr int U = D / 8;
       for (int u = threadIdx.x; u < a.rows * U; u += C::THREADS)
-        reduce_unit<D>(a, base, n, b, g, u / U, (u % U) * 8);
+        reduce_unit<D, true>(a, base, n, b, g, u / U, (u % U) * 8);
       if (threadIdx.x == 0) a.counters[pair] = 0;
     }
   }
