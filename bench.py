@@ -28,7 +28,9 @@ KV-cache append (the write side, pa_cache_append) at a decode-sized shape (C4's
 32 sequences x 4 new tokens, latency-bound) and at two prefill-sized shapes
 (HBM-bound), with the same flush and events. `decode_loop` times back-to-back
 decode steps (context bump, append, plan, decode) launched eagerly, replayed
-as one graph per step, and unrolled eight to a graph.
+as one graph per step, and unrolled eight to a graph, and with one plan for
+eight steps. `prefill` times the chunked-prefill shapes (192 and 256 query
+rows per kv head, one K/V pass) against the HBM and bf16 MFMA rooflines.
 
 `--scale-sweep` replaces the step bench with a sweep of the partition kernel
 over context lengths scaled 1/8 .. 2x, fitting time = fixed + bytes / rate per
@@ -128,6 +130,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle sample")
     p.add_argument("--no-append", action="store_true", help="skip the KV-cache append timings")
+    p.add_argument("--no-prefill", action="store_true",
+                   help="skip the chunked-prefill timings (many query rows per kv head)")
     p.add_argument("--no-loop", action="store_true",
                    help="skip the decode-loop timings (eager vs graph-captured steps)")
     p.add_argument("--scale-sweep", action="store_true",
@@ -343,6 +347,7 @@ def main():
         torch.cuda.empty_cache()
 
     append = None if args.no_append else append_bench(args, flush)
+    prefill = None if args.no_prefill else prefill_bench(args, flush)
     loops = None if args.no_loop else decode_loop_bench(args)
 
     head = HEADLINE if HEADLINE in results else names[0]
@@ -412,6 +417,7 @@ def main():
         "parity_sample": parity,
         "per_config": results,
         "append": append,
+        "prefill": prefill,
         "decode_loop": loops,
     }
     print(json.dumps(line), flush=True)
@@ -476,6 +482,77 @@ def append_bench(args, flush):
         log(f"append {name}: {rows} rows, {nbytes} bytes in {t:.1f} us -> {nbytes / t / 1e3:.0f} GB/s")
         del nk, nv, kc, vc, sc
     torch.cuda.empty_cache()
+    return res
+
+
+def prefill_bench(args, flush):
+    """pa_decode on the chunked-prefill shapes (workloads.PREFILL: 192 and 256
+    query rows per kv head, which one kernel serves while reading each K/V
+    chunk once), plan built beforehand, median of HIP-event samples after a
+    read flush. Reported against both rooflines: KV bytes / time against
+    8 TB/s, and the algorithmic MFMA flops (QK^T and PV over every visible key
+    of every row, 4 * head_dim flops per row and key) / time against the bf16
+    dense peak of 2.5 PFLOP/s."""
+    import numpy as np
+    import torch
+
+    import paged_attention_decode_block_amd as pa
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    cus = pa.pa_query_device(0)
+    res = {}
+    for name, spec in W.PREFILL.items():
+        if args.only and name not in args.only.split(","):
+            continue
+        w = W.generate(spec, args.seed)
+        d = {k: getattr(w, k).to(dev) for k in ("q", "k_cache", "v_cache", "block_table",
+                                                 "context_lens")}
+        kvs = None if w.kv_scales is None else w.kv_scales.to(dev)
+        mode = {W.SCALE_NONE: pa.PA_SCALE_NONE, W.SCALE_PER_TENSOR: pa.PA_SCALE_PER_TENSOR,
+                W.SCALE_PER_TOKEN_HEAD: pa.PA_SCALE_PER_TOKEN_HEAD}[spec.kv_scale_mode]
+        dims = pa.make_dims(batch=spec.batch, q_len=spec.q_len, num_q_heads=spec.num_q_heads,
+                            num_kv_heads=spec.num_kv_heads, head_dim=spec.head_dim,
+                            page_size=spec.page_size, num_pages=w.num_pages,
+                            max_pages_per_seq=spec.max_pages_per_seq,
+                            kv_dtype=pa.PA_KV_FP8_E4M3FN if spec.kv_dtype == W.KV_FP8
+                            else pa.PA_KV_BF16, kv_scale_mode=mode,
+                            partition_size=spec.partition_size)
+        ws = torch.empty(pa.pa_workspace_bytes(dims, cus), dtype=torch.uint8, device=dev)
+        out = torch.empty_like(d["q"])
+        plan = pa.pa_plan(dims, d["context_lens"], workspace=ws)
+        us = []
+        for it in range(args.warmup + args.steps):
+            if flush is not None:
+                flush()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            pa.pa_decode(plan, d["q"], d["k_cache"], d["v_cache"], d["block_table"],
+                         d["context_lens"], spec.q_len, spec.scale, mode, kvs, out)
+            e1.record()
+            torch.cuda.synchronize()
+            if it >= args.warmup:
+                us.append(e0.elapsed_time(e1) * 1e3)
+        assert pa.pa_plan_status(plan) == 0, f"prefill {name}: device status"
+        t = statistics.median(us)
+        ctx = w.context_lens.numpy().astype(np.int64)
+        # keys seen by query i of sequence b: ctx_b - q_len + i + 1
+        keys = int(sum(spec.q_len * (c - spec.q_len) + spec.q_len * (spec.q_len + 1) // 2
+                       for c in ctx))
+        flops = 4 * spec.head_dim * spec.num_q_heads * keys
+        kvb = w.kv_bytes()
+        res[name] = {"rows_per_kv_head": spec.rows, "q_block": int(plan.c.q_block),
+                     "kv_passes": -(-spec.q_len // int(plan.c.q_block)),
+                     "us": round(t, 2), "kv_bytes": kvb,
+                     "GBps": round(kvb / t / 1e3, 1),
+                     "frac_of_hbm_peak": round(kvb / t / 1e3 / HBM_PEAK_GBS, 4),
+                     "mfma_flops": flops, "TFLOPs": round(flops / t / 1e6, 1),
+                     "frac_of_bf16_mfma_peak": round(flops / t / 1e6 / 2500.0, 4)}
+        log(f"prefill {name}: {spec.rows} rows per kv head, {res[name]['kv_passes']} K/V pass(es), "
+            f"{t:.1f} us -> {kvb / t / 1e3:.0f} GB/s, {flops / t / 1e6:.0f} TFLOP/s")
+        del d, kvs, ws, out, w
+        torch.cuda.empty_cache()
     return res
 
 

@@ -116,12 +116,13 @@ enum {
 typedef struct pa_dims {
   int32_t batch;
   int32_t q_len;               /* appended query tokens per sequence, >= 1.
-                                  When the rows per kv head, q_len *
-                                  (num_q_heads / num_kv_heads), exceed what one
-                                  kernel holds (64 at head_dim 128, 32 at 256),
-                                  the queries go in blocks of q_block (each
-                                  block a work list and launches of its own);
-                                  one query's rows must fit, else
+                                  Up to 256 rows per kv head, q_len *
+                                  (num_q_heads / num_kv_heads), at head_dim 128
+                                  (64 at 256) run in one kernel, which reads
+                                  each K/V chunk once for all of them; past
+                                  that the queries go in blocks of q_block
+                                  (each block a work list and launches of its
+                                  own); one query's rows must fit, else
                                   PA_ERR_UNSUPPORTED                         */
   int32_t num_q_heads;
   int32_t num_kv_heads;        /* divides num_q_heads                        */

@@ -45,6 +45,7 @@ int log2i(int x) {
 }
 
 constexpr int kDefaultPartition = 256;
+constexpr int kMaxKernelRows = 256;  // query rows per kv head the widest instantiation holds
 constexpr int kMaxGridMultiplier = 16;
 constexpr int kMaxDevices = 64;
 
@@ -156,8 +157,8 @@ int check_dims(const pa_dims* in, pa_dims* out, int* variant, bool need_decode =
     // whose rows one does, each block decoded as its own work list
     const int64_t group = d.num_q_heads / d.num_kv_heads;
     qb = 0;
-    for (int q = static_cast<int>(std::min<int64_t>(d.q_len, 64)); q >= 1 && qb == 0; --q) {
-      if (q * group > 64) continue;
+    for (int q = static_cast<int>(std::min<int64_t>(d.q_len, kMaxKernelRows)); q >= 1 && qb == 0; --q) {
+      if (q * group > kMaxKernelRows) continue;
       v = pa::pick_variant(d.head_dim, d.kv_dtype == PA_KV_FP8_E4M3FN, d.kv_scale_mode,
                            static_cast<int>(q * group), d.page_size, d.partition_size);
       if (v >= 0) qb = q;

@@ -550,14 +550,17 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
   constexpr int NST = NW / RS;  // chunk streams
   static_assert(NS == 2 || NS == 3, "2 or 3 K/V register stages");
   static_assert(NW % RS == 0, "waves split evenly over streams");
-  // SH: the RS waves of a stream share the chunk through LDS. Each loads and
-  // widens its share of it (wave r: 2 NB / RS blocks of K for even r, of V
-  // for odd r) into the stream's bf16 K and V tiles; after a workgroup
-  // barrier every wave reads K and V from the tiles. The tiles alternate
-  // between two buffers by step; a segment merge puts the waves' O tiles in
-  // the stream's two buffers (its first barrier follows every read of them).
-  static_assert(!SH || ((RS == 2 || (RS == 4 && NB % 2 == 0)) && FP8),
-                "shared tiles: 2 or 4 waves per fp8 stream");
+  // SH: the RS waves of a stream share the chunk through LDS. Each loads its
+  // share of it (wave r: 2 NB / RS blocks of K for even r, of V for odd r),
+  // widens fp8 to bf16, and writes it into the stream's bf16 K and V tiles;
+  // after a workgroup barrier every wave reads K and V from the tiles for its
+  // own rows. So one K/V read serves RS * RT * 16 query rows (up to 256: the
+  // long queries of a chunked prefill read the cache once). The tiles
+  // alternate between two buffers by step; a segment merge puts the waves' O
+  // tiles in the stream's two buffers (its first barrier follows every read
+  // of them).
+  static_assert(!SH || (RS % 2 == 0 && (2 * NB) % RS == 0),
+                "shared tiles: an even number of waves, each loading whole blocks");
   constexpr int SHR = SH ? RS : 0;
   constexpr int NBL = Stage<D, FP8, NB, SM, SHR>::NBL;
   constexpr int SHBUF = 2 * C::VBYTES;  // one buffer: K tile, then V tile
@@ -702,8 +705,12 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
 #pragma unroll
           for (int i = 0; i < LPB; ++i) {
             const u32x4 wv = cs.k[b][i];
-            *reinterpret_cast<bf16x8*>(row + 128 * i + 32 * j) = fp8x8_to_bf16(wv.x, wv.y);
-            *reinterpret_cast<bf16x8*>(row + 128 * i + 32 * j + 16) = fp8x8_to_bf16(wv.z, wv.w);
+            if constexpr (FP8) {
+              *reinterpret_cast<bf16x8*>(row + 128 * i + 32 * j) = fp8x8_to_bf16(wv.x, wv.y);
+              *reinterpret_cast<bf16x8*>(row + 128 * i + 32 * j + 16) = fp8x8_to_bf16(wv.z, wv.w);
+            } else {
+              *reinterpret_cast<u32x4*>(row + 64 * i + 16 * j) = wv;
+            }
           }
         }
       }
@@ -1147,6 +1154,16 @@ const VariantEntry kVariants[] = {
     PA_V(128, 1, 2, 1, 2, 8, 2, 1, 1), PA_V(128, 1, 2, 2, 2, 8, 2, 1, 1), PA_VS(128, 1, 2, 2, 2, 8, 2, 2, 1),
     PA_V(256, 1, 1, 1, 2, 4, 3, 1, 0), PA_V(256, 1, 1, 2, 1, 4, 2, 1, 0),
     PA_V(256, 1, 2, 1, 2, 4, 3, 1, 0), PA_V(256, 1, 2, 2, 1, 4, 2, 1, 0),
+    // long queries (chunked prefill): 128 or 256 rows per kv head at head
+    // dim 128, 64 at 256, all sharing one read of each chunk
+    PA_VS(128, 0, 0, 2, 2, 8, 2, 4, 0), PA_VS(128, 0, 0, 2, 2, 8, 2, 4, 1),
+    PA_VS(128, 0, 0, 2, 4, 8, 2, 8, 0), PA_VS(128, 0, 0, 2, 4, 8, 2, 8, 1),
+    PA_VS(128, 1, 1, 2, 2, 8, 2, 4, 0), PA_VS(128, 1, 1, 2, 2, 8, 2, 4, 1),
+    PA_VS(128, 1, 1, 2, 4, 8, 2, 8, 0), PA_VS(128, 1, 1, 2, 4, 8, 2, 8, 1),
+    PA_VS(128, 1, 2, 2, 2, 8, 2, 4, 0), PA_VS(128, 1, 2, 2, 2, 8, 2, 4, 1),
+    PA_VS(128, 1, 2, 2, 4, 8, 2, 8, 0), PA_VS(128, 1, 2, 2, 4, 8, 2, 8, 1),
+    PA_VS(256, 0, 0, 1, 2, 8, 2, 4, 0), PA_VS(256, 1, 1, 1, 2, 8, 2, 4, 0),
+    PA_VS(256, 1, 2, 1, 2, 8, 2, 4, 0),
 };
 #undef PA_V
 #undef PA_VS

@@ -57,9 +57,9 @@ def _dims(**kw):
     (dict(kv_dtype=2), pa.PA_ERR_UNSUPPORTED),
     (dict(kv_scale_mode=pa.PA_SCALE_PER_TENSOR), pa.PA_ERR_SCALE_MODE),
     (dict(kv_dtype=pa.PA_KV_FP8_E4M3FN), pa.PA_ERR_SCALE_MODE),
-    # one query's rows past what a kernel holds (64 at head_dim 128, 32 at 256)
-    (dict(q_len=1, num_q_heads=128, num_kv_heads=1), pa.PA_ERR_UNSUPPORTED),
-    (dict(head_dim=256, q_len=2, num_q_heads=64, num_kv_heads=1), pa.PA_ERR_UNSUPPORTED),
+    # one query's rows past what a kernel holds (256 at head_dim 128, 64 at 256)
+    (dict(q_len=1, num_q_heads=512, num_kv_heads=1), pa.PA_ERR_UNSUPPORTED),
+    (dict(head_dim=256, q_len=2, num_q_heads=128, num_kv_heads=1), pa.PA_ERR_UNSUPPORTED),
 ])
 def test_dims_rejected_on_host(kw, code):
     with pytest.raises(pa.PaError) as e:
@@ -73,16 +73,16 @@ def test_dims_rejected_on_host(kw, code):
 
 
 def test_long_queries_take_one_workspace_block_per_query_block():
-    # 16 rows per query: four queries (64 rows) fit one kernel at head_dim 128,
-    # so 5 and 8 queries take two blocks of four, 9 take three; at head_dim 256
-    # (32 rows) blocks hold two queries
-    one = pa.pa_workspace_bytes(_dims(q_len=4, num_q_heads=16, num_kv_heads=1), 256)
+    # 16 rows per query: sixteen queries (256 rows) fit one kernel at head_dim
+    # 128, so 17 and 32 queries take two blocks of sixteen, 33 take three; at
+    # head_dim 256 (64 rows) blocks hold four queries
+    one = pa.pa_workspace_bytes(_dims(q_len=16, num_q_heads=16, num_kv_heads=1), 256)
     assert one % 256 == 0
-    for q_len, blocks in ((5, 2), (8, 2), (9, 3)):
+    for q_len, blocks in ((17, 2), (32, 2), (33, 3)):
         ws = pa.pa_workspace_bytes(_dims(q_len=q_len, num_q_heads=16, num_kv_heads=1), 256)
         assert ws == blocks * one, (q_len, ws, one)
-    one256 = pa.pa_workspace_bytes(_dims(head_dim=256, q_len=2, num_q_heads=16, num_kv_heads=1), 256)
-    assert pa.pa_workspace_bytes(_dims(head_dim=256, q_len=7, num_q_heads=16, num_kv_heads=1),
+    one256 = pa.pa_workspace_bytes(_dims(head_dim=256, q_len=4, num_q_heads=16, num_kv_heads=1), 256)
+    assert pa.pa_workspace_bytes(_dims(head_dim=256, q_len=13, num_q_heads=16, num_kv_heads=1),
                                  256) == 4 * one256
 
 

@@ -47,6 +47,17 @@ CASES = {
                                                   ctx_hi=700, max_ctx=768), None),
     "fp8 per-token q4 page 32 partition 48": (W.scaled(W.C4_Q4_TOK, batch=3, page_size=32,
                                                        ctx_lo=4, ctx_hi=500, max_ctx=512), 48),
+    # shared tiles for long queries: 4 or 8 waves share each chunk (bf16 and fp8)
+    "bf16 D128 page 16, 128 rows shared": (W.scaled(W.C3, batch=3, q_len=32, ctx_lo=32,
+                                                    ctx_hi=400, max_ctx=512), None),
+    "bf16 D128 page 128, 256 rows shared": (W.scaled(W.C2, batch=3, q_len=16, ctx_lo=16,
+                                                     ctx_hi=600, max_ctx=640, pool_pages=0,
+                                                     pool_slack=0.3), None),
+    "fp8 per-token q16 page 1024, 256 rows shared": (W.scaled(W.C4_Q4_TOK, batch=2, q_len=16,
+                                                              ctx_lo=16, ctx_hi=2500,
+                                                              max_ctx=3072), None),
+    "bf16 D256 page 32, 64 rows shared": (W.scaled(W.C5, batch=2, q_len=4, ctx_lo=8, ctx_hi=700,
+                                                   max_ctx=1024, pool_slack=0.2), None),
     # head_dim 256
     "bf16 D256 page 32": (W.scaled(W.C5, batch=2, ctx_lo=8, ctx_hi=700, max_ctx=1024,
                                    pool_slack=0.2), None),

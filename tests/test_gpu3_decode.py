@@ -77,14 +77,21 @@ def test_page_sizes(ps):
 @pytest.mark.parametrize("q_len,hq,hkv,d", [(1, 8, 8, 128), (2, 8, 2, 128), (3, 16, 1, 128),
                                             (1, 32, 1, 128), (2, 32, 1, 128), (4, 12, 1, 128),
                                             (8, 4, 4, 256), (2, 16, 2, 256), (4, 8, 1, 256),
-                                            (3, 10, 1, 256)])
+                                            (3, 10, 1, 256),
+                                            # shared-tile instantiations: 65..256 rows at
+                                            # head_dim 128, 33..64 at 256, one pass
+                                            (5, 16, 1, 128), (8, 16, 1, 128), (12, 16, 1, 128),
+                                            (16, 16, 1, 128), (9, 20, 2, 128), (5, 8, 1, 256),
+                                            (16, 4, 1, 256)])
 def test_row_shapes(q_len, hq, hkv, d):
-    # rows per kv head R = q_len * hq / hkv from 1 to 64: one to four 16-row tiles
+    # rows per kv head R = q_len * hq / hkv from 1 to 256: one to sixteen 16-row
+    # tiles, all in one kernel
     spec = W.Spec(f"rows_{q_len}x{hq}/{hkv}_d{d}", 3, q_len, hq, hkv, d, 32, q_len, 700,
                   max_ctx=1024)
     w = W.generate(spec, 2026)
     say(f"[decode] {spec.name} ctx={w.context_lens.tolist()}")
-    out, _ = run(w)
+    out, plan = run(w)
+    assert plan.c.q_block == q_len
     check(w, out, spec.name)
 
 
@@ -210,29 +217,38 @@ def test_pages_beyond_4_gib(kv):
 
 
 LONG_Q = {
-    # name: (q_len, Hq, Hkv, D, kv dtype, scale mode); rows = q_len * Hq / Hkv
-    "q5_g16_d128": (5, 16, 1, 128, W.KV_BF16, W.SCALE_NONE),           # 80 rows: blocks of 4 + 1
-    "q24_g8_d128": (24, 8, 1, 128, W.KV_BF16, W.SCALE_NONE),           # 192 rows: 3 blocks of 8
-    "q40_g1_d256": (40, 4, 4, 256, W.KV_BF16, W.SCALE_NONE),           # 40 rows: 32 + 8
-    "q8_g16_fp8_tok": (8, 16, 1, 128, W.KV_FP8, W.SCALE_PER_TOKEN_HEAD),  # 128 rows: 2 blocks
-    "q9_g16_fp8_ten": (9, 16, 1, 128, W.KV_FP8, W.SCALE_PER_TENSOR),      # 144 rows: 4 + 4 + 1
+    # name: (q_len, Hq, Hkv, D, kv dtype, scale mode); rows = q_len * Hq / Hkv. Up to
+    # 256 rows (64 at head_dim 256) one kernel reads each chunk once for all of
+    # them; past that the queries go in blocks.
+    "q5_g16_d128": (5, 16, 1, 128, W.KV_BF16, W.SCALE_NONE),           # 80 rows: one pass
+    "q24_g8_d128": (24, 8, 1, 128, W.KV_BF16, W.SCALE_NONE),           # 192 rows: one pass
+    "q40_g1_d256": (40, 4, 4, 256, W.KV_BF16, W.SCALE_NONE),           # 40 rows: one pass
+    "q8_g16_fp8_tok": (8, 16, 1, 128, W.KV_FP8, W.SCALE_PER_TOKEN_HEAD),  # 128 rows: one pass
+    "q9_g16_fp8_ten": (9, 16, 1, 128, W.KV_FP8, W.SCALE_PER_TENSOR),      # 144 rows: one pass
+    "q20_g16_d128": (20, 16, 1, 128, W.KV_BF16, W.SCALE_NONE),         # 320 rows: 16 + 4 queries
+    "q33_g8_fp8_tok": (33, 8, 1, 128, W.KV_FP8, W.SCALE_PER_TOKEN_HEAD),  # 264 rows: 32 + 1
+    "q40_g4_d256": (40, 8, 2, 256, W.KV_BF16, W.SCALE_NONE),           # 160 rows: 4 blocks of 16 + 8
 }
 
 
 @pytest.mark.parametrize("name", list(LONG_Q))
-def test_long_queries_in_blocks(name):
-    """More query rows per kv head than one kernel holds: the queries are
-    decoded in blocks, each with the keys up to its own last query (chunked
-    prefill of q_len tokens). Contexts include the shortest, ctx = q_len."""
+def test_long_queries(name):
+    """Many query rows per kv head (chunked prefill of q_len tokens): one
+    kernel serves up to 256 rows (64 at head_dim 256), its waves sharing each
+    K/V chunk through LDS; past that the queries are decoded in blocks, each
+    with the keys up to its own last query. Contexts include the shortest,
+    ctx = q_len."""
     q_len, hq, hkv, d, kvd, mode = LONG_Q[name]
     ps = 1024 if kvd == W.KV_FP8 else 32
     spec = W.Spec(name, 4, q_len, hq, hkv, d, ps, q_len, 1500, kv_dtype=kvd, kv_scale_mode=mode,
                   max_ctx=2048)
     ctxs = [q_len, q_len + 1, 700, 1500]
     w = W.generate(spec, 2029, context_lens=ctxs)
-    say(f"[decode] long q {name} ctx={ctxs}")
+    rows = q_len * hq // hkv
+    say(f"[decode] long q {name} ({rows} rows) ctx={ctxs}")
     out, plan = run(w)
-    assert plan.c.q_block < q_len
+    fits = rows <= (256 if d == 128 else 64)
+    assert (plan.c.q_block == q_len) == fits, (plan.c.q_block, q_len)
     assert pa.pa_plan_status(plan) == 0
     check(w, out, name)
 
@@ -241,7 +257,7 @@ def test_long_queries_past_the_plan_lds_tables():
     """Query blocks over a batch whose plan tables do not fit in LDS (more
     than 8192 sequences): each block's work list comes from the table kernel
     and the items kernel. A sample of sequences is compared with the oracle."""
-    spec = W.Spec("long_q_8200", 8200, 5, 16, 1, 128, 32, 5, 64, max_ctx=64, pool_slack=0.0)
+    spec = W.Spec("long_q_8200", 8200, 20, 16, 1, 128, 32, 20, 64, max_ctx=64, pool_slack=0.0)
     w = W.generate(spec, 2039)
     say(f"[decode] long q, {spec.batch} sequences, {int(w.context_lens.sum())} tokens")
     out, plan = run(w)
@@ -259,10 +275,11 @@ def test_long_queries_past_the_plan_lds_tables():
 
 
 def test_long_queries_bad_context_reports():
-    spec = W.Spec("long_q_bad", 2, 9, 16, 1, 128, 32, 9, 300, max_ctx=512)
-    w = W.generate(spec, 2026, context_lens=[9, 300])
-    w.context_lens[0] = 8                            # shorter than q_len
+    spec = W.Spec("long_q_bad", 2, 20, 16, 1, 128, 32, 20, 300, max_ctx=512)
+    w = W.generate(spec, 2026, context_lens=[20, 300])
+    w.context_lens[0] = 19                           # shorter than q_len
     out, plan = run(w)
+    assert plan.c.q_block < spec.q_len
     assert pa.pa_plan_status(plan) == pa.PA_DEV_BAD_CONTEXT
 
 

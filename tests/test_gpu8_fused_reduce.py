@@ -30,6 +30,8 @@ SPECS = {
     "fp8_tok_d256": W.scaled(W.C5, batch=2, ctx_lo=300, ctx_hi=1500, max_ctx=1536,
                              pool_slack=0.2, kv_dtype=W.KV_FP8,
                              kv_scale_mode=W.SCALE_PER_TOKEN_HEAD),
+    # 192 rows per kv head: the shared-tile instantiation of 8 waves per chunk
+    "bf16_q24_g8": W.Spec("bf16_q24_g8", 3, 24, 8, 1, 128, 32, 24, 1500, max_ctx=2048),
 }
 
 
@@ -89,10 +91,11 @@ def test_fused_one_pair_over_every_workgroup(kv):
 
 
 def test_fused_with_query_blocks():
-    """q_len 9 x 16 rows: three query blocks, each with its own counters."""
-    spec = W.Spec("long_q_fused", 4, 9, 16, 1, 128, 1024, 9, 1500, kv_dtype=W.KV_FP8,
+    """q_len 20 x 16 rows: two query blocks (16 + 4 queries), each with its own
+    counters."""
+    spec = W.Spec("long_q_fused", 4, 20, 16, 1, 128, 1024, 20, 1500, kv_dtype=W.KV_FP8,
                   kv_scale_mode=W.SCALE_PER_TENSOR, max_ctx=2048)
-    w = W.generate(spec, 2029, context_lens=[9, 10, 700, 1500])
+    w = W.generate(spec, 2029, context_lens=[20, 21, 700, 1500])
     d = upload(w)
     (sep,), _ = _decode(w, d, SEPARATE, 64)
     fused, plan = _decode(w, d, FUSED, 64, reps=2)

@@ -115,6 +115,14 @@ C4_Q4_TEN = dataclasses.replace(C4_Q1_TEN, name="C4_fp8_q4_per_tensor", q_len=4)
 C5 = Spec("C5_long_ctx_d256", 4, 8, 16, 16, 256, 32, 65536, 65536, pool_slack=0.0)
 
 CONFIGS = {s.name: s for s in (C1, C2, C3, C4_Q1_TOK, C4_Q4_TOK, C4_Q1_TEN, C4_Q4_TEN, C5)}
+
+# Chunked-prefill shapes (many query rows per kv head; not among the decode
+# workloads above): the batched GQA heads and contexts with a 48-token chunk
+# (192 rows per kv head), and the fp8 per-token heads and contexts with a
+# 16-token chunk (256 rows).
+P1 = dataclasses.replace(C3, name="P1_prefill_gqa_q48", q_len=48)
+P2 = dataclasses.replace(C4_Q1_TOK, name="P2_prefill_fp8_q16", q_len=16)
+PREFILL = {s.name: s for s in (P1, P2)}
 SEEDS = (2026, 2029, 2039)
 
 
