@@ -22,10 +22,11 @@
 //     of the pair's query rows on them (RS > 1 splits many rows over waves
 //     so that each wave's registers allow two waves per SIMD)
 //   * each wave runs an NS-stage software pipeline over its chunk stream:
-//     the K/V rows of chunk i + NS - 1 (16-byte buffer loads straight into
-//     MFMA operand registers) are issued while chunk i is computed, and the
-//     block-table entries that address them were loaded NS - 1 chunks before
-//     that, so no wait for an entry ever drains the K/V loads in flight
+//     the K/V rows of chunk i + NS - 1 (16-byte non-temporal buffer loads,
+//     each wave instruction reading 1 KB contiguous) are issued while chunk i
+//     is computed, and the block-table entries that address them were loaded
+//     NS - 1 chunks before that, so no wait for an entry ever drains the K/V
+//     loads in flight; the rows then go through LDS into MFMA operand order
 //   * S^T = K Q^T on MFMA 16x16x32 bf16 (K rows are the A operand as loaded;
 //     fp8 K is decoded to bf16 exactly); fp32 online softmax in the exp2
 //     domain with the causal mask of the appended tokens; O^T += V^T P^T on
@@ -142,7 +143,7 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const uint8_t* p) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
-template <int D, bool FP8, int RT, int NB, int NW>
+template <int D, bool FP8, int RT, int NB, int NW, bool LIN = false>
 struct Cfg {
   static constexpr int KVB = FP8 ? 1 : 2;      // bytes per cache element
   static constexpr int ROWB = D * KVB;         // bytes per cache row
@@ -155,7 +156,10 @@ struct Cfg {
   static constexpr int VBYTES = TC * VROW;
   static constexpr int OROW = D + 4;           // floats per row of the merge tile
   static constexpr int OBYTES = 16 * OROW * 4;
-  static constexpr int WBYTES = VBYTES > OBYTES ? VBYTES : OBYTES;
+  // a wave's private LDS: its V tile (and, with linear loads, its K tile in
+  // front of it), which the merge's O tile reuses
+  static constexpr int TBYTES = (LIN ? 2 : 1) * VBYTES;
+  static constexpr int WBYTES = TBYTES > OBYTES ? TBYTES : OBYTES;
   static constexpr int THREADS = NW * 64;
   static_assert(ROWB % 64 == 0, "row must be a multiple of 64 bytes");
   static_assert(NB == 1 || NB % 2 == 0, "blocks per chunk: 1 or even");
@@ -197,6 +201,38 @@ __device__ __forceinline__ uint64_t uni64(uint64_t v) {
 template <bool STREAM = false>
 __device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t voff) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, STREAM ? 2 : 0));
+}
+
+// Two lane layouts of a 16-row block of ROWB-byte cache rows, for the
+// 16-byte K/V loads:
+//  * rows layout: load i of lane (c = lane % 16, j = lane / 16) covers bytes
+//    [64 i + 16 j, +16) of row c, so each lane holds MFMA operand pieces of
+//    one token row; one load touches 64 bytes of each of 16 rows;
+//  * linear layout (LIN): load i of lane l covers bytes [1024 i + 16 l, +16)
+//    of the block, row (64 i + l) / (ROWB / 16), so one load reads 1 KB
+//    contiguous. HBM serves this layout markedly faster (a streaming probe on
+//    MI355X: 7.0-7.2 TB/s with non-temporal loads, against 6.0-6.3 TB/s for
+//    the rows layout), and LDS puts the rows in operand order afterwards.
+template <int ROWB>
+__device__ __forceinline__ int lin_row(int i, int lane) { return (64 * i + lane) / (ROWB / 16); }
+template <int ROWB>
+__device__ __forceinline__ int lin_col(int i, int lane) { return (16 * (64 * i + lane)) % ROWB; }
+
+// The rows of block blk of a chunk, as loaded in the linear layout, into a
+// bf16 LDS tile of VROW-byte rows (fp8 widened exactly to bf16).
+template <bool FP8, int ROWB, int LPB, int VROW>
+__device__ __forceinline__ void lin_to_tile(uint8_t* tile, int blk, const u32x4 (&w)[LPB], int lane) {
+#pragma unroll
+  for (int i = 0; i < LPB; ++i) {
+    uint8_t* dst = tile + (16 * blk + lin_row<ROWB>(i, lane)) * VROW;
+    const int col = lin_col<ROWB>(i, lane);
+    if constexpr (FP8) {
+      *reinterpret_cast<bf16x8*>(dst + 2 * col) = fp8x8_to_bf16(w[i].x, w[i].y);
+      *reinterpret_cast<bf16x8*>(dst + 2 * col + 16) = fp8x8_to_bf16(w[i].z, w[i].w);
+    } else {
+      *reinterpret_cast<u32x4*>(dst + col) = w[i];
+    }
+  }
 }
 
 template <int D, bool FP8, int NB, int SM, int SHR = 0>
@@ -319,11 +355,19 @@ __device__ __forceinline__ void load_pages(const DecodeArgs& a, const Entry& e, 
   }
 }
 
-template <int D, bool FP8, int NB, int SM, bool OPC, int SHR = 0>
+template <int D, bool FP8, int NB, int SM, bool OPC, int SHR = 0, bool LIN = false>
 __device__ __forceinline__ void issue_kv(const DecodeArgs& a, const Entry& e, const uint32_t (&pgv)[NB],
                                          Stage<D, FP8, NB, SM, SHR>& st, int lane, int rsub = 0) {
   constexpr bool SH = SHR != 0;
   constexpr int ROWB = D * (FP8 ? 1 : 2);
+  // non-temporal policy (each byte is read once): bf16 caches always, fp8
+  // ones with the linear layout
+  constexpr bool NT = !FP8 || LIN;
+  // byte offset of load i of this lane inside a 16-row block
+  const auto lo = [&](int i) -> uint32_t {
+    return LIN ? static_cast<uint32_t>(1024 * i + 16 * lane)
+               : static_cast<uint32_t>((lane & 15) * ROWB + 16 * (lane >> 4) + 64 * i);
+  };
   constexpr int NBL = Stage<D, FP8, NB, SM, SHR>::NBL;
   // SH: wave r of the stream loads NBL blocks of K (even r) or V (odd r),
   // starting at block (r / 2) NBL
@@ -346,11 +390,10 @@ __device__ __forceinline__ void issue_kv(const DecodeArgs& a, const Entry& e, co
     const uint64_t row0 = uni64(cache_row(page, e.g(), e.tc0 & ps_mask, a.num_kv_heads, a.ps_log2));
     const rsrc_t rk = make_rsrc(kbase + row0 * ROWB, static_cast<uint32_t>(nl * ROWB));
     const rsrc_t rv = make_rsrc(a.v_cache + row0 * ROWB, static_cast<uint32_t>(nl * ROWB));
-    const uint32_t lane_off = static_cast<uint32_t>(c * ROWB + 16 * j);
 #pragma unroll
     for (int b = 0; b < NBL; ++b)
 #pragma unroll
-      for (int i = 0; i < LPB; ++i) st.k[b][i] = bload16<!FP8>(rk, lane_off + 16 * ROWB * (blk0 + b) + 64 * i);
+      for (int i = 0; i < LPB; ++i) st.k[b][i] = bload16<NT>(rk, 16 * ROWB * (blk0 + b) + lo(i));
     if constexpr (SM == PA_SCALE_PER_TOKEN_HEAD) {
       const rsrc_t rks = make_rsrc(a.kv_scales + row0, static_cast<uint32_t>(nl * 4));
 #pragma unroll
@@ -362,7 +405,7 @@ __device__ __forceinline__ void issue_kv(const DecodeArgs& a, const Entry& e, co
 #pragma unroll
       for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
-        for (int i = 0; i < LPB; ++i) st.v[blk][i] = bload16<!FP8>(rv, lane_off + 16 * ROWB * blk + 64 * i);
+        for (int i = 0; i < LPB; ++i) st.v[blk][i] = bload16<NT>(rv, 16 * ROWB * blk + lo(i));
     }
     if constexpr (SM == PA_SCALE_PER_TOKEN_HEAD) {
       const uint64_t vplane = static_cast<uint64_t>(a.num_pages) * a.num_kv_heads << a.ps_log2;
@@ -374,9 +417,8 @@ __device__ __forceinline__ void issue_kv(const DecodeArgs& a, const Entry& e, co
     }
     return;
   }
-  // Lane (c, j) reads bytes [64 i + 16 j, +16) of row c of each 16-token
-  // block; the block's resource covers only its rows before the segment end.
-  const uint32_t lane_off = static_cast<uint32_t>(c * ROWB + 16 * j);
+  // Each 16-token block's resource covers only its rows before the segment
+  // end; loads follow the lane layout (rows or linear).
   rsrc_t rk[NB], rv[NB];
   uint64_t row0[NB];
   int32_t nlive[NB];
@@ -401,7 +443,7 @@ __device__ __forceinline__ void issue_kv(const DecodeArgs& a, const Entry& e, co
 #pragma unroll
   for (int b = 0; b < NBL; ++b)
 #pragma unroll
-    for (int i = 0; i < LPB; ++i) st.k[b][i] = bload16<!FP8>(rk[SH ? blk0 + b : b], lane_off + 64 * i);
+    for (int i = 0; i < LPB; ++i) st.k[b][i] = bload16<NT>(rk[SH ? blk0 + b : b], lo(i));
   if constexpr (SM == PA_SCALE_PER_TOKEN_HEAD) {
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk) {
@@ -413,7 +455,7 @@ __device__ __forceinline__ void issue_kv(const DecodeArgs& a, const Entry& e, co
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
-      for (int i = 0; i < LPB; ++i) st.v[blk][i] = bload16<!FP8>(rv[blk], lane_off + 64 * i);
+      for (int i = 0; i < LPB; ++i) st.v[blk][i] = bload16<NT>(rv[blk], lo(i));
   }
   if constexpr (SM == PA_SCALE_PER_TOKEN_HEAD) {
     const uint64_t vplane = static_cast<uint64_t>(a.num_pages) * a.num_kv_heads << a.ps_log2;
@@ -543,9 +585,12 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(DecodeArgs a) {
 }
 
 template <int D, bool FP8, int SM, int RT, int NB, int NW, int NS, int RS, bool OPC, bool SH,
-          bool FUSED>
+          bool FUSED, bool LIN>
 __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(DecodeArgs a) {
-  using C = Cfg<D, FP8, RT, NB, NW>;
+  // LIN: K/V loaded in the linear lane layout and put in operand order
+  // through LDS (private K and V tiles per wave, or the stream's shared tiles)
+  using C = Cfg<D, FP8, RT, NB, NW, LIN && !SH>;
+  constexpr int ROWB = D * (FP8 ? 1 : 2);
   constexpr int KC = C::KC, DT = C::DT, TC = C::TC, LPB = C::LPB;
   constexpr int NST = NW / RS;  // chunk streams
   static_assert(NS == 2 || NS == 3, "2 or 3 K/V register stages");
@@ -655,7 +700,7 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
 #pragma unroll
   for (int k = 0; k < NS - 1; ++k) {
     load_pages<NB, OPC>(a, ev[NS - 1 + k], pg[pslot(NS - 1 + k)]);
-    issue_kv<D, FP8, NB, SM, OPC, SHR>(a, ev[k], pg[pslot(k)], st[k], lane, rsub);
+    issue_kv<D, FP8, NB, SM, OPC, SHR, LIN>(a, ev[k], pg[pslot(k)], st[k], lane, rsub);
   }
 
   float m[RT], l[RT];
@@ -689,16 +734,31 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
     if constexpr (QPF) {
       if (ev[1].live() && ev[1].first()) load_q<D, FP8, RT>(a, ev[1], lane, qrow0, qn);
     }
-    issue_kv<D, FP8, NB, SM, OPC, SHR>(a, ev[NS - 1], pg[(CUR + 1) % NS], st[ISS], lane, rsub);
+    issue_kv<D, FP8, NB, SM, OPC, SHR, LIN>(a, ev[NS - 1], pg[(CUR + 1) % NS], st[ISS], lane, rsub);
 
     // SH: this wave's share of the chunk, widened, into the stream's tiles;
     // every wave meets the barrier once per step
-    uint8_t* const ktile = SH ? sh_buf(stream, par) : nullptr;
-    uint8_t* const vtile = SH ? sh_buf(stream, par) + C::VBYTES : wlds;
+    uint8_t* const ktile = SH ? sh_buf(stream, par) : wlds;
+    uint8_t* const vtile = SH ? sh_buf(stream, par) + C::VBYTES : (LIN ? wlds + C::VBYTES : wlds);
+    if constexpr (!SH && LIN) {
+      // this wave's chunk, in operand order, into its private K and V tiles
+      // (a wave's LDS accesses complete in order: no barrier)
+      if (e0.data()) {
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) {
+          lin_to_tile<FP8, ROWB, LPB, C::VROW>(ktile, blk, cs.k[blk], lane);
+          lin_to_tile<FP8, ROWB, LPB, C::VROW>(vtile, blk, cs.v[blk], lane);
+        }
+      }
+    }
     if constexpr (SH) {
       if (e0.data()) {
         uint8_t* const mine = sh_buf(stream, par) + (rsub & 1) * C::VBYTES;
         const int blk0 = (rsub >> 1) * NBL;
+        if constexpr (LIN) {
+#pragma unroll
+          for (int b = 0; b < NBL; ++b) lin_to_tile<FP8, ROWB, LPB, C::VROW>(mine, blk0 + b, cs.k[b], lane);
+        } else
 #pragma unroll
         for (int b = 0; b < NBL; ++b) {
           uint8_t* row = mine + (16 * (blk0 + b) + c) * C::VROW;
@@ -728,7 +788,7 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
           bf16x8 kf;
-          if constexpr (SH) {
+          if constexpr (SH || LIN) {
             kf = *reinterpret_cast<const bf16x8*>(ktile + (16 * blk + c) * C::VROW +
                                                   2 * qk_dim<FP8>(kc, j));
           } else if constexpr (FP8) {
@@ -805,9 +865,9 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
         l[rt] += ps;
       }
 
-      // ---- V rows -> wave-private LDS tile (row-major bf16); SH: already
-      // in the stream's tile
-      if constexpr (!SH) {
+      // ---- V rows -> wave-private LDS tile (row-major bf16); SH, LIN:
+      // already in the tile
+      if constexpr (!SH && !LIN) {
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk) {
           uint8_t* vrow = wlds + (16 * blk + c) * C::VROW;
@@ -1020,15 +1080,16 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
 // (s, y) takes segment s of the plan (with the live context length, as the
 // partition pass does) and its chunks y, y + gridDim.y, ...; for each it runs
 // load_pages and issue_kv of one instantiation, exactly as a chunk stream
-// entry would, and writes the registers back out in the layout the math
-// reads them in: lane (c, j) holds bytes [64 i + 16 j, +16) of row
-// 16 blk + c of the chunk, and per-token scales of token 16 blk + 4 j + c % 4.
+// entry would, and writes the registers back out by the lane layout the math
+// takes them in (load i of a lane holds the row and bytes lin_row / lin_col
+// give, or in the rows layout bytes [64 i + 16 j, +16) of row 16 blk + c),
+// and per-token scales of token 16 blk + 4 j + c % 4.
 // Rows t < te go to [pair][t] of k_out / v_out / scales_out; rows past the
 // segment's end must have loaded as zeros, and any that did not set
 // PA_DEV_DEBUG_DEAD_ROW. With shared tiles (SHR waves per stream) wave r of
 // the workgroup loads its share: K (even r) or V (odd r), blocks from
 // (r / 2) * NBL.
-template <int D, bool FP8, int SM, int NB, bool OPC, int SHR>
+template <int D, bool FP8, int SM, int NB, bool OPC, int SHR, bool LIN>
 __global__ __launch_bounds__(64 * (SHR ? SHR : 1)) void loader_kernel(DecodeArgs a, uint8_t* k_out,
                                                                       uint8_t* v_out, float* s_out) {
   constexpr int ROWB = D * (FP8 ? 1 : 2);
@@ -1058,18 +1119,19 @@ __global__ __launch_bounds__(64 * (SHR ? SHR : 1)) void loader_kernel(DecodeArgs
     uint32_t pg[NB];
     load_pages<NB, OPC>(a, e, pg);
     Stage<D, FP8, NB, SM, SHR> st = {};
-    issue_kv<D, FP8, NB, SM, OPC, SHR>(a, e, pg, st, lane, rsub);
+    issue_kv<D, FP8, NB, SM, OPC, SHR, LIN>(a, e, pg, st, lane, rsub);
+    // load i of this lane: row and byte of the block (rows or linear layout)
     const auto put = [&](uint8_t* out, int blk, const u32x4 (&w)[LPB]) {
-      const int32_t t = e.tc0 + 16 * blk + c;
-      if (t < te) {
 #pragma unroll
-        for (int i = 0; i < LPB; ++i)
-          *reinterpret_cast<u32x4*>(out + (base + t) * ROWB + 64 * i + 16 * j) = w[i];
-      } else {
-        uint32_t any = 0;
-#pragma unroll
-        for (int i = 0; i < LPB; ++i) any |= w[i].x | w[i].y | w[i].z | w[i].w;
-        if (any) atomicOr(a.status + ST_BITS, PA_DEV_DEBUG_DEAD_ROW);
+      for (int i = 0; i < LPB; ++i) {
+        const int row = LIN ? lin_row<ROWB>(i, lane) : c;
+        const int col = LIN ? lin_col<ROWB>(i, lane) : 64 * i + 16 * j;
+        const int32_t t = e.tc0 + 16 * blk + row;
+        if (t < te) {
+          *reinterpret_cast<u32x4*>(out + (base + t) * ROWB + col) = w[i];
+        } else if (w[i].x | w[i].y | w[i].z | w[i].w) {
+          atomicOr(a.status + ST_BITS, PA_DEV_DEBUG_DEAD_ROW);
+        }
       }
     };
     if constexpr (SH) {
@@ -1101,26 +1163,26 @@ __global__ __launch_bounds__(64 * (SHR ? SHR : 1)) void loader_kernel(DecodeArgs
   }
 }
 
-template <int D, bool FP8, int SM, int NB, bool OPC, int SHR>
+template <int D, bool FP8, int SM, int NB, bool OPC, int SHR, bool LIN>
 hipError_t launch_loader_t(const DecodeArgs& a, int max_segs, uint8_t* k_out, uint8_t* v_out,
                            float* s_out, hipStream_t s) {
   const int chunks = (a.capacity + 16 * NB - 1) / (16 * NB);
   const dim3 grid(max_segs, chunks < 1024 ? chunks : 1024);
-  hipLaunchKernelGGL((loader_kernel<D, FP8, SM, NB, OPC, SHR>), grid, dim3(64 * (SHR ? SHR : 1)), 0, s,
-                     a, k_out, v_out, s_out);
+  hipLaunchKernelGGL((loader_kernel<D, FP8, SM, NB, OPC, SHR, LIN>), grid, dim3(64 * (SHR ? SHR : 1)),
+                     0, s, a, k_out, v_out, s_out);
   return hipGetLastError();
 }
 
-template <int D, bool FP8, int SM, int RT, int NB, int NW, int NS, int RS, bool OPC, bool SH>
+template <int D, bool FP8, int SM, int RT, int NB, int NW, int NS, int RS, bool OPC, bool SH, bool LIN>
 hipError_t launch_partition_t(const DecodeArgs& a, int grid, hipStream_t s) {
   // the fused reduce is an instantiation of its own, so the separate-reduce
   // kernels carry none of its code
   if (a.counters != nullptr)
-    hipLaunchKernelGGL((partition_kernel<D, FP8, SM, RT, NB, NW, NS, RS, OPC, SH, true>), dim3(grid),
-                       dim3(NW * 64), 0, s, a);
+    hipLaunchKernelGGL((partition_kernel<D, FP8, SM, RT, NB, NW, NS, RS, OPC, SH, true, LIN>),
+                       dim3(grid), dim3(NW * 64), 0, s, a);
   else
-    hipLaunchKernelGGL((partition_kernel<D, FP8, SM, RT, NB, NW, NS, RS, OPC, SH, false>), dim3(grid),
-                       dim3(NW * 64), 0, s, a);
+    hipLaunchKernelGGL((partition_kernel<D, FP8, SM, RT, NB, NW, NS, RS, OPC, SH, false, LIN>),
+                       dim3(grid), dim3(NW * 64), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1133,14 +1195,19 @@ struct VariantEntry {
   LoaderFn loader;  // the same instantiation's page loader, alone (test support)
 };
 
+// K/V lane layout of every instantiation: linear (1 KB contiguous per load)
+#ifndef PA_LINEAR_LOADS
+#define PA_LINEAR_LOADS 1
+#endif
+constexpr bool kLin = PA_LINEAR_LOADS != 0;
 #define PA_V(D, F, SM, RT, NB, NW, NS, RS, OPC)                                                  \
   {{D, F, SM, RT * RS, NB, NW, NS, OPC, 0},                                                      \
-   launch_partition_t<D, F != 0, SM, RT, NB, NW, NS, RS, OPC != 0, false>,                      \
-   launch_loader_t<D, F != 0, SM, NB, OPC != 0, 0>}
+   launch_partition_t<D, F != 0, SM, RT, NB, NW, NS, RS, OPC != 0, false, kLin>,                \
+   launch_loader_t<D, F != 0, SM, NB, OPC != 0, 0, kLin>}
 #define PA_VS(D, F, SM, RT, NB, NW, NS, RS, OPC)                                                 \
   {{D, F, SM, RT * RS, NB, NW, NS, OPC, RS},                                                     \
-   launch_partition_t<D, F != 0, SM, RT, NB, NW, NS, RS, OPC != 0, true>,                       \
-   launch_loader_t<D, F != 0, SM, NB, OPC != 0, RS>}
+   launch_partition_t<D, F != 0, SM, RT, NB, NW, NS, RS, OPC != 0, true, kLin>,                 \
+   launch_loader_t<D, F != 0, SM, NB, OPC != 0, RS, kLin>}
 const VariantEntry kVariants[] = {
     // head dim, fp8, scale mode, row tiles per wave, 16-token blocks per
     // chunk, waves, K/V stages, waves per chunk stream, one page per chunk;
