@@ -148,6 +148,9 @@ def parse():
     p.add_argument("--tune-margin", type=float, default=0.02,
                    help="a setting other than the default must be faster by this fraction, "
                         "in graph replays and in eager launches alike")
+    p.add_argument("--read-probe", action="store_true",
+                   help="instead of the step bench: HBM read rate of the K/V load layouts alone "
+                        "(pa_debug_read_probe) over a 4 GiB buffer, contiguous and page-scattered")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run one 512 MiB device copy first (a known-size kernel for scaling "
                         "rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -208,6 +211,9 @@ def main():
         return
     if args.tune:
         tune(args, flush)
+        return
+    if args.read_probe:
+        read_probe(args)
         return
     if args.calibrate_copy:
         src = torch.ones(1 << 27, dtype=torch.float32, device=dev)
@@ -697,6 +703,56 @@ def plan_sweep(args, flush):
         del ws, ctx
     print(json.dumps({"metric": "pa_plan time vs batch size", "unit": "us", "steps": args.steps,
                       "warmup": args.warmup, "points": points}), flush=True)
+
+
+def read_probe(args):
+    """HBM read rate of the partition pass's two K/V lane layouts, alone
+    (pa_debug_read_probe): 16-row blocks of 128, 256 and 512-byte rows (fp8
+    and bf16 rows at head_dim 128 and 256) read from a 4 GiB buffer with
+    non-temporal 16-byte loads, in block order (contiguous) and in a seeded
+    random permutation (page-scattered, as a block table places pages), by 4
+    and 8 waves per CU; median of 10 HIP-event timings after 2 warm-ups.
+    Prints one JSON line."""
+    import torch
+
+    import paged_attention_decode_block_amd as pa
+
+    dev = torch.device("cuda:0")
+    cus = pa.pa_query_device(0)
+    total = 4 << 30
+    buf = torch.ones(total, dtype=torch.uint8, device=dev)
+    sink = torch.empty(cus * 16 * 64, dtype=torch.float32, device=dev)
+    gen = torch.Generator(device="cpu").manual_seed(args.seed)
+    points = []
+    for row_bytes in (128, 256, 512):
+        nblk = total // (16 * row_bytes)
+        orders = {"contiguous": torch.arange(nblk, dtype=torch.int32),
+                  "page-scattered": torch.randperm(nblk, generator=gen, dtype=torch.int32)}
+        for order, blocks_h in orders.items():
+            blocks = blocks_h.to(dev)
+            for waves in (4, 8):
+                per = nblk // (cus * waves) // 2 * 2
+                nbytes = per * cus * waves * 16 * row_bytes
+                rate = {}
+                for linear in (True, False):
+                    ts = []
+                    for it in range(12):
+                        e0 = torch.cuda.Event(enable_timing=True)
+                        e1 = torch.cuda.Event(enable_timing=True)
+                        e0.record()
+                        pa.pa_debug_read_probe(buf, blocks, row_bytes, linear, waves, sink)
+                        e1.record()
+                        e1.synchronize()
+                        if it >= 2:
+                            ts.append(e0.elapsed_time(e1) * 1e3)
+                    rate["linear" if linear else "rows"] = round(nbytes / statistics.median(ts) / 1e3, 1)
+                points.append({"row_bytes": row_bytes, "block_bytes": 16 * row_bytes, "order": order,
+                               "waves_per_cu": waves, "bytes": nbytes, "GBps": rate})
+                log(f"read probe {row_bytes} B rows, {order}, {waves} waves: linear "
+                    f"{rate['linear']:.0f} GB/s, rows {rate['rows']:.0f} GB/s")
+            del blocks
+    print(json.dumps({"metric": "HBM read rate of the K/V load layouts (non-temporal 16-byte loads)",
+                      "unit": "GB/s", "peak": HBM_PEAK_GBS, "points": points}), flush=True)
 
 
 def tune(args, flush):

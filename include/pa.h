@@ -359,6 +359,25 @@ int pa_decode_static(const pa_dims* dims, const void* q, const void* k_cache, co
 /* Size in bytes of pa_decode_static's per-device scratch. */
 uint64_t pa_static_scratch_bytes(void);
 
+/* Measurement support: the HBM read rate of the partition pass's K/V load
+ * layouts, alone. Reads blocks of 16 rows of row_bytes bytes (a 16-token block
+ * of one cache page and kv head: 128 = fp8 at head_dim 128, 256 = bf16 at
+ * 128 or fp8 at 256, 512 = bf16 at 256) from `buffer` with 16-byte
+ * non-temporal loads, in the linear lane layout (linear != 0: each load
+ * instruction reads 1 KB contiguous) or the rows layout (64 bytes of each of
+ * 16 rows). The grid has one workgroup of `waves` waves per CU; wave w reads
+ * blocks[w * per + k] for k < per = num_blocks / (CUs * waves), rounded down
+ * to even, two blocks at a time. Block indices are clamped to the buffer's
+ * blocks. sink (device float[CUs * waves * 64]) receives one value per lane
+ * so the loads are kept. buffer, blocks (device int32[num_blocks]) and sink
+ * are device memory. Asynchronous; time it with events on `stream`. Errors:
+ * PA_ERR_NULL, PA_ERR_UNSUPPORTED (row_bytes), PA_ERR_DIMS (waves outside
+ * [1, 16], buffer smaller than one block), PA_ERR_ALIGN, PA_ERR_DEVICE,
+ * PA_ERR_HIP. */
+int pa_debug_read_probe(const void* buffer, uint64_t buffer_bytes, const int32_t* blocks,
+                        int32_t num_blocks, int32_t row_bytes, int32_t linear, int32_t waves,
+                        float* sink, void* stream);
+
 /* Static text for a PA_* status code. */
 const char* pa_status_string(int status);
 

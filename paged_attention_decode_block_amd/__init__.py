@@ -118,6 +118,7 @@ def lib() -> ctypes.CDLL:
             "pa_decode_static": (ctypes.c_int, [P(pa_dims), vp, vp, vp, vp, vp, i32,
                                                 ctypes.c_float, i32, vp, vp, P(pa_plan_t), vp]),
             "pa_static_scratch_bytes": (u64, []),
+            "pa_debug_read_probe": (ctypes.c_int, [vp, u64, vp, i32, i32, i32, i32, vp, vp]),
             "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "pa_last_error": (ctypes.c_char_p, []),
         }
@@ -379,6 +380,19 @@ def pa_cache_append(dims: pa_dims, new_k, new_v, block_table, context_lens, k_ca
     _on(None, context_lens=context_lens, new_k=new_k, new_v=new_v, block_table=block_table,
         k_cache=k_cache, v_cache=v_cache, kv_scales=kv_scales, device_status=device_status)
     _check(lib().pa_cache_append(ctypes.byref(dims), *ptrs, _stream(stream)))
+
+
+def pa_debug_read_probe(buffer, blocks, row_bytes: int, linear: bool, waves: int, sink,
+                        stream=None):
+    """Read 16-row blocks of `buffer` in one K/V lane layout (include/pa.h,
+    pa_debug_read_probe): measurement support for the load layout."""
+    _buf(buffer, "buffer", (torch.uint8,))
+    _buf(blocks, "blocks", _I32)
+    _buf(sink, "sink", _F32)
+    _on(None, buffer=buffer, blocks=blocks, sink=sink)
+    _check(lib().pa_debug_read_probe(_ptr(buffer), buffer.numel(), _ptr(blocks), blocks.numel(),
+                                     row_bytes, int(bool(linear)), waves, _ptr(sink),
+                                     _stream(stream)))
 
 
 def pa_status_string(code: int) -> str:

@@ -670,6 +670,29 @@ int pa_decode_static(const pa_dims* dims, const void* q, const void* k_cache, co
 
 uint64_t pa_static_scratch_bytes(void) { return kStaticScratchBytes; }
 
+int pa_debug_read_probe(const void* buffer, uint64_t buffer_bytes, const int32_t* blocks,
+                        int32_t num_blocks, int32_t row_bytes, int32_t linear, int32_t waves,
+                        float* sink, void* stream) {
+  if (!buffer || !blocks || !sink) return fail(PA_ERR_NULL, "buffer, blocks and sink are required");
+  if (row_bytes != 128 && row_bytes != 256 && row_bytes != 512)
+    return fail(PA_ERR_UNSUPPORTED, "row_bytes %d is not 128, 256 or 512", row_bytes);
+  if (waves < 1 || waves > 16) return fail(PA_ERR_DIMS, "waves %d outside [1, 16]", waves);
+  if (!aligned(buffer, 16) || !aligned(blocks, 4) || !aligned(sink, 4))
+    return fail(PA_ERR_ALIGN, "buffer must be 16-byte aligned, blocks and sink 4-byte aligned");
+  const uint64_t nbuf = buffer_bytes / (16ull * row_bytes);
+  if (nbuf < 1 || nbuf > (1ull << 31) - 1 || num_blocks < 0)
+    return fail(PA_ERR_DIMS, "buffer holds %llu blocks; 1 to 2^31 - 1 are supported",
+                static_cast<unsigned long long>(nbuf));
+  int dev = -1;
+  if (int rc = current_device(&dev)) return rc;
+  int32_t cus = 0;
+  if (int rc = pa_query_device(dev, &cus)) return rc;
+  return hip_check(pa::launch_read_probe(static_cast<const uint8_t*>(buffer), static_cast<int32_t>(nbuf),
+                                         blocks, num_blocks, row_bytes, linear != 0, cus, waves, sink,
+                                         static_cast<hipStream_t>(stream)),
+                   "read probe launch") ?: ok();
+}
+
 const char* pa_status_string(int status) {
   switch (status) {
     case PA_OK: return "PA_OK";

@@ -86,4 +86,10 @@ hipError_t launch_reduce(const DecodeArgs& a, int head_dim, int num_pairs, hipSt
 hipError_t launch_loader(int variant, const DecodeArgs& a, int max_segs, uint8_t* k_out,
                          uint8_t* v_out, float* scales_out, hipStream_t s);
 
+// Measurement support (pa_probe.hip): read num_blocks / (grid * waves)
+// (rounded down to even) blocks of 16 rows of row_bytes bytes per wave, in the
+// linear or the rows lane layout; block indices clamped to [0, nbuf).
+hipError_t launch_read_probe(const uint8_t* buf, int32_t nbuf, const int32_t* blocks, int32_t num_blocks,
+                             int row_bytes, bool linear, int grid, int waves, float* sink, hipStream_t s);
+
 }  // namespace pa
