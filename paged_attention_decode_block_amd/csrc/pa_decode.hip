@@ -196,8 +196,8 @@ __device__ __forceinline__ uint64_t uni64(uint64_t v) {
 }
 
 // 16-byte buffer load. STREAM sets the non-temporal cache policy (each K/V
-// byte is read once): measured 1-4% faster for bf16 caches and 7-8% slower
-// for fp8 ones, so only bf16 K/V loads use it.
+// byte is read once). In the rows layout it was 1-4% faster for bf16 caches
+// and 7-8% slower for fp8 ones; in the linear layout both dtypes take it.
 template <bool STREAM = false>
 __device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t voff) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, STREAM ? 2 : 0));
