@@ -1,9 +1,9 @@
 """Full-size workloads in the launch configuration bench.py times.
 
-Every output must be finite and the device status clean; a sample of whole
-sequences (the first, the last, the longest and the one with the smallest
-partial tail) is compared with the CPU oracle element by element, each
-sequence attended on its own.
+Every output must be finite and the device status clean, and every sequence
+is compared with the CPU oracle element by element, each sequence attended on
+its own (the oracle takes well under a second per sequence, 65,536-token ones
+included, on a 16-thread host).
 """
 import numpy as np
 import pytest
@@ -21,16 +21,23 @@ FULL = ["C1_tiny", "C2_single_seq", "C3_batched_gqa", "C4_fp8_q1_per_token",
         "C5_long_ctx_d256"]
 
 
-def _sample(ctx, P):
-    ctx = list(ctx)
-    picks = {0, len(ctx) - 1, int(np.argmax(ctx)),
-             min(range(len(ctx)), key=lambda b: (ctx[b] % P) or P)}
-    return sorted(picks)
+def _check_every_sequence(w, got, label):
+    spec = w.spec
+    worst = 0.0
+    for b in range(spec.batch):
+        want, _ = oracle.decode(w.q[b:b + 1], w.k_cache, w.v_cache, w.block_table[b:b + 1],
+                                w.context_lens[b:b + 1], spec.q_len, spec.scale, spec.page_size,
+                                spec.kv_dtype, spec.kv_scale_mode, w.kv_scales)
+        err = assert_close(got[b:b + 1], want, tol(spec), f"{label} sequence {b}")
+        worst = max(worst, err)
+        if b % 8 == 0 or b == spec.batch - 1:
+            say(f"[{label}] sequence {b} (ctx {int(w.context_lens[b])}): max abs err {err:.2e}")
+    say(f"[{label}] all {spec.batch} sequences: max abs err {worst:.2e}")
 
 
 @pytest.mark.timeout(300)
 @pytest.mark.parametrize("name", FULL)
-def test_full_size_sampled_parity(name):
+def test_full_size_parity(name):
     spec = W.CONFIGS[name]
     w = W.generate(spec, 2026)
     say(f"[full] {name}: {spec.batch} sequences, {int(w.context_lens.sum())} tokens")
@@ -38,12 +45,7 @@ def test_full_size_sampled_parity(name):
     assert pa.pa_plan_status(plan) == 0
     got = to_f64(out)
     assert np.isfinite(got).all()
-    for b in _sample(w.context_lens.tolist(), spec.partition_size):
-        want, _ = oracle.decode(w.q[b:b + 1], w.k_cache, w.v_cache, w.block_table[b:b + 1],
-                                w.context_lens[b:b + 1], spec.q_len, spec.scale, spec.page_size,
-                                spec.kv_dtype, spec.kv_scale_mode, w.kv_scales)
-        err = assert_close(got[b:b + 1], want, tol(spec), f"{name} sequence {b}")
-        say(f"[full] {name} sequence {b} (ctx {int(w.context_lens[b])}): max abs err {err:.2e}")
+    _check_every_sequence(w, got, f"full {name}")
 
 
 # twice the context lengths of three workloads (the largest shapes bench.py's
@@ -54,7 +56,7 @@ DOUBLED = ["C3_batched_gqa", "C4_fp8_q1_per_token", "C4_fp8_q4_per_token"]
 
 @pytest.mark.timeout(300)
 @pytest.mark.parametrize("name", DOUBLED)
-def test_doubled_contexts_sampled_parity(name):
+def test_doubled_contexts_parity(name):
     base = W.CONFIGS[name]
     spec = W.scaled(base, ctx_lo=2 * base.ctx_lo, ctx_hi=2 * base.ctx_hi, max_ctx=0)
     w = W.generate(spec, 2029)
@@ -64,9 +66,4 @@ def test_doubled_contexts_sampled_parity(name):
     assert pa.pa_plan_status(plan) == 0
     got = to_f64(out)
     assert np.isfinite(got).all()
-    for b in _sample(w.context_lens.tolist(), spec.partition_size):
-        want, _ = oracle.decode(w.q[b:b + 1], w.k_cache, w.v_cache, w.block_table[b:b + 1],
-                                w.context_lens[b:b + 1], spec.q_len, spec.scale, spec.page_size,
-                                spec.kv_dtype, spec.kv_scale_mode, w.kv_scales)
-        err = assert_close(got[b:b + 1], want, tol(spec), f"{name} x2 sequence {b}")
-        say(f"[full x2] {name} sequence {b} (ctx {int(w.context_lens[b])}): max abs err {err:.2e}")
+    _check_every_sequence(w, got, f"full x2 {name}")
