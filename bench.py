@@ -151,6 +151,9 @@ def parse():
     p.add_argument("--read-probe", action="store_true",
                    help="instead of the step bench: HBM read rate of the K/V load layouts alone "
                         "(pa_debug_read_probe) over a 4 GiB buffer, contiguous and page-scattered")
+    p.add_argument("--prefill-only", action="store_true",
+                   help="instead of the step bench: only the chunked-prefill timings (one JSON "
+                        "line), e.g. for counter runs over those kernels alone")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run one 512 MiB device copy first (a known-size kernel for scaling "
                         "rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -223,6 +226,11 @@ def main():
         torch.cuda.synchronize()
         log("calibration copy: 536870912 bytes read, 536870912 bytes written")
         del src, dst
+    if args.prefill_only:
+        print(json.dumps({"metric": "chunked-prefill pa_decode: KV GB/s and MFMA TFLOP/s, 1 GPU",
+                          "steps": args.steps, "warmup": args.warmup,
+                          "prefill": prefill_bench(args, flush)}), flush=True)
+        return
     results = {}
     keep = {}
     for name in names:
