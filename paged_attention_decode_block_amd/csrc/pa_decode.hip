@@ -572,9 +572,10 @@ constexpr int kReduceRows = 16;
 template <int D>
 __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(DecodeArgs a) {
   const int p = blockIdx.x;
+  // both loads go out before the first wait
   const int n = ldu(a.nseg, p);
-  if (n <= 1) return;
   const int base = ldu(a.seg_base, p);
+  if (n <= 1) return;
   const int b = p / a.num_kv_heads;
   const int g = p - b * a.num_kv_heads;
   constexpr int U = D / 8;  // 8-dim units per row
@@ -1049,6 +1050,10 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
   // needed, and the waits sit after the last K/V loads.
   if constexpr (FUSED) {
     if (pend0 < 0) return;
+    // segment counts and slot bases of the pending pairs: scalar loads whose
+    // latency overlaps the wait for the partial stores
+    const int n0 = ldu(a.nseg, pend0), base0 = ldu(a.seg_base, pend0);
+    const int n1 = pend1 >= 0 ? ldu(a.nseg, pend1) : 0, base1 = pend1 >= 0 ? ldu(a.seg_base, pend1) : 0;
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     if (wave == 0) {
@@ -1057,7 +1062,7 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
         const int32_t pair = lane == 0 ? pend0 : pend1;
         const int32_t before = __hip_atomic_fetch_add(a.counters + pair, 1, __ATOMIC_RELAXED,
                                                       __HIP_MEMORY_SCOPE_AGENT);
-        s_last[lane] = before == ldu(a.nseg, pair) - 1 ? 1 : 0;
+        s_last[lane] = before == (lane == 0 ? n0 : n1) - 1 ? 1 : 0;
       }
     }
     __syncthreads();
@@ -1066,8 +1071,8 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
       if (pair < 0 || !s_last[k]) continue;
       const int b = pair / a.num_kv_heads;
       const int g = pair - b * a.num_kv_heads;
-      const int n = ldu(a.nseg, pair);
-      const int base = ldu(a.seg_base, pair);
+      const int n = k == 0 ? n0 : n1;
+      const int base = k == 0 ? base0 : base1;
       constexpr int U = D / 8;
       for (int u = threadIdx.x; u < a.rows * U; u += C::THREADS)
         reduce_unit<D, true>(a, base, n, b, g, u / U, (u % U) * 8);
