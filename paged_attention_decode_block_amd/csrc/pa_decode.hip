@@ -1200,7 +1200,10 @@ struct VariantEntry {
   LoaderFn loader;  // the same instantiation's page loader, alone (test support)
 };
 
-// K/V lane layout of every instantiation: linear (1 KB contiguous per load)
+// K/V lane layout of every instantiation: linear (1 KB contiguous per load).
+// Building with -DPA_LINEAR_LOADS=0 selects the rows layout instead, for
+// measuring one against the other; the library's build and its tests use the
+// linear layout only.
 #ifndef PA_LINEAR_LOADS
 #define PA_LINEAR_LOADS 1
 #endif
