@@ -390,6 +390,12 @@ def pa_debug_read_probe(buffer, blocks, row_bytes: int, linear: bool, waves: int
     _buf(blocks, "blocks", _I32)
     _buf(sink, "sink", _F32)
     _on(None, buffer=buffer, blocks=blocks, sink=sink)
+    if not 1 <= waves <= 16:
+        raise PaError(PA_ERR_DIMS, f"waves {waves} outside [1, 16]")
+    need = pa_query_device(sink.device.index) * waves * 64
+    if sink.numel() < need:
+        raise PaError(PA_ERR_DIMS, f"sink holds {sink.numel()} floats; one per lane of the grid, "
+                                   f"{need}, is needed")
     _check(lib().pa_debug_read_probe(_ptr(buffer), buffer.numel(), _ptr(blocks), blocks.numel(),
                                      row_bytes, int(bool(linear)), waves, _ptr(sink),
                                      _stream(stream)))
