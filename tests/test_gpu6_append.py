@@ -91,6 +91,38 @@ CASES = {
 }
 
 
+def _random_case(i):
+    import random
+    r = random.Random(9100 + i)
+    ps = r.choice([16, 32, 64, 128, 256, 512, 1024])
+    q_len = r.choice([1, 1, 2, 3, 4, 8, 16])
+    maxp = max(r.randint(1, 6), -(-q_len // ps))
+    fp8 = r.random() < 0.6
+    mode = (r.choice([pa.PA_SCALE_PER_TOKEN_HEAD, pa.PA_SCALE_PER_TENSOR]) if fp8
+            else pa.PA_SCALE_NONE)
+    return (r.randint(1, 7), q_len, r.choice([1, 2, 4, 8, 16]), r.choice([128, 256]), ps, maxp,
+            fp8, mode)
+
+
+@pytest.mark.parametrize("i", range(32))
+def test_append_random_shapes_bitwise(i):
+    """Seeded random shapes (batch, q_len, kv heads, head_dim, page size,
+    capacity, dtype and scale mode drawn together), cache bytes and scales
+    bit for bit against the oracle."""
+    B, q_len, Hkv, D, ps, maxp, fp8, mode = _random_case(i)
+    nk, nv, bt, ctx, kc, vc, sc, num_pages = _draw(300 + i, B, q_len, Hkv, D, ps, maxp, fp8, mode)
+    say(f"[append random {i}] B={B} q_len={q_len} Hkv={Hkv} D={D} page={ps} maxp={maxp} "
+        f"fp8={fp8} mode={mode} ctx={ctx.tolist()}")
+    dims = _dims(B, q_len, Hkv, D, ps, num_pages, maxp, fp8, mode)
+    gk, gv, gs, st = _gpu_append(dims, nk, nv, bt, ctx, kc, vc, sc)
+    wk, wv, ws, wst = cache.append(nk, nv, bt, ctx, q_len, ps, kc, vc, fp8,
+                                   mode == pa.PA_SCALE_PER_TOKEN_HEAD, sc)
+    assert st == wst == 0
+    assert np.array_equal(gk, wk) and np.array_equal(gv, wv)
+    if ws is not None:
+        assert np.array_equal(gs.view(np.uint32), ws.view(np.uint32))
+
+
 @pytest.mark.parametrize("name", list(CASES))
 def test_append_matches_oracle_bitwise(name):
     B, q_len, Hkv, D, ps, maxp, fp8, mode = CASES[name]
