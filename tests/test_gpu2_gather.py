@@ -125,6 +125,41 @@ def test_loader_bitwise(name):
     _compare(w, w.context_lens.tolist(), k_out, v_out, s_out, name)
 
 
+def _random_spec(i):
+    import random
+    r = random.Random(8100 + i)
+    hkv = r.choice([1, 2, 4, 8])
+    group = r.choice([1, 2, 4, 8, 16])
+    q_len = r.choice([1, 1, 2, 4, 8])
+    ps = r.choice([16, 32, 64, 128, 256, 512, 1024])
+    fp8 = r.random() < 0.5
+    mode = r.choice([W.SCALE_PER_TOKEN_HEAD, W.SCALE_PER_TENSOR]) if fp8 else W.SCALE_NONE
+    batch = r.randint(1, 5)
+    cap = max(r.randint(1, max(1, 3072 // ps)) * ps, q_len)
+    ctx = [r.choice([q_len, cap, r.randint(q_len, cap)]) for _ in range(batch)]
+    spec = W.Spec(f"loader_rand{i}", batch, q_len, hkv * group, hkv, r.choice([128, 256]), ps,
+                  min(ctx), max(ctx), kv_dtype=W.KV_FP8 if fp8 else W.KV_BF16,
+                  kv_scale_mode=mode, max_ctx=cap)
+    return spec, ctx, r.choice([16, 32, 48, 64, 256, 1024])
+
+
+@pytest.mark.parametrize("i", range(32))
+def test_loader_random_shapes_bitwise(i):
+    """Seeded random shapes (kv heads, group, q_len, head_dim, page size,
+    capacity, dtype and scale mode, partition size drawn together): whichever
+    instantiation the decode picks, its loader reads exactly the oracle's
+    rows and scales."""
+    spec, ctx, partition = _random_spec(i)
+    w = W.generate(spec, 4100 + i, context_lens=ctx)
+    say(f"[gather random {i}] B={spec.batch} q_len={spec.q_len} Hq={spec.num_q_heads} "
+        f"Hkv={spec.num_kv_heads} D={spec.head_dim} page={spec.page_size} {spec.kv_dtype}/"
+        f"{spec.kv_scale_mode} cap={spec.max_ctx} ctx={ctx} P={partition}")
+    d = upload(w)
+    status, k_out, v_out, s_out = _gather(w, d, d.context_lens, partition)
+    assert status == 0, f"device status {status}"
+    _compare(w, ctx, k_out, v_out, s_out, f"random case {i}")
+
+
 @pytest.mark.parametrize("name", ["bf16 D128 page 16", "fp8 per-token q1 page 1024",
                                   "fp8 per-token q4 page 1024 shared"])
 def test_loader_reads_live_context_lengths(name):
