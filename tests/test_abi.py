@@ -267,3 +267,44 @@ def test_binding_rejects_host_context_lens_before_planning():
     with pytest.raises(pa.PaError) as e:
         pa.pa_plan(_dims(), torch.ones(3, dtype=torch.int32))
     assert e.value.code == pa.PA_ERR_DIMS
+
+
+def test_host_calls_from_many_threads_keep_their_own_errors():
+    """The host entry points run concurrently from several threads (ctypes
+    releases the GIL for each call): every thread gets the same answers as a
+    lone caller, and pa_last_error reports the calling thread's own last
+    failure, not another thread's."""
+    import threading
+
+    good = [pa.make_dims(batch=b, q_len=q, num_q_heads=16, num_kv_heads=h, head_dim=d, page_size=ps,
+                         num_pages=64, max_pages_per_seq=8)
+            for b, q, h, d, ps in [(1, 1, 1, 128, 128), (64, 1, 8, 128, 16), (4, 8, 16, 256, 32),
+                                   (32, 4, 1, 128, 1024), (7, 3, 2, 128, 64)]]
+    want_bytes = [pa.pa_workspace_bytes(d_, 256) for d_ in good]
+    want_choice = [tuple(getattr(pa.pa_plan_choice(d_, 256), f) for f, _ in pa.pa_dims._fields_)
+                   for d_ in good]
+    errors = []
+
+    def worker(t):
+        try:
+            for it in range(200):
+                i = (t + it) % len(good)
+                assert pa.pa_workspace_bytes(good[i], 256) == want_bytes[i]
+                got = pa.pa_plan_choice(good[i], 256)
+                assert tuple(getattr(got, f) for f, _ in pa.pa_dims._fields_) == want_choice[i]
+                # a failure whose message names this thread's own bad head_dim
+                bad = pa.make_dims(batch=1, q_len=1, num_q_heads=1, num_kv_heads=1,
+                                   head_dim=1000 + t, page_size=16, num_pages=1, max_pages_per_seq=1)
+                with pytest.raises(pa.PaError) as e:
+                    pa.pa_workspace_bytes(bad, 256)
+                assert e.value.code == pa.PA_ERR_UNSUPPORTED
+                assert f"head_dim {1000 + t} " in e.value.text, e.value.text
+        except BaseException as ex:  # reported by the main thread
+            errors.append((t, repr(ex)))
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(8)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors

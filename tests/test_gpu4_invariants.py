@@ -195,3 +195,40 @@ def _same_cache(w: W.Workload, spec: W.Spec) -> W.Workload:
                 sc[:, dst, :, t % ps] = w.kv_scales[:, src, :, t % ps0]
         nxt += pages[b]
     return W.Workload(spec, w.seed, w.q, k, v, bt, w.context_lens, sc, npool)
+
+
+def test_decodes_on_concurrent_streams_match_sequential_ones():
+    """Plans and decodes of three workloads issued on three streams at once,
+    each with its own workspace and output, several rounds without a sync in
+    between: every output is bitwise the one the same call gives alone on
+    the default stream. (The library keeps no state between calls but the
+    caller's workspaces, so nothing may leak across streams.)"""
+    names = sorted(SPECS)
+    ws_, ds, refs = {}, {}, {}
+    for name in names:
+        w = W.generate(SPECS[name], 2039)
+        d = upload(w)
+        ref, _ = run(w, d)
+        ws_[name], ds[name], refs[name] = w, d, ref
+    torch.cuda.synchronize()
+    streams = {name: torch.cuda.Stream() for name in names}
+    outs = {name: [] for name in names}
+    say("[inv] three streams at once")
+    for st in streams.values():
+        st.wait_stream(torch.cuda.current_stream())
+    for rnd in range(4):
+        for name in names:
+            w, d, s = ws_[name], ds[name], ws_[name].spec
+            with torch.cuda.stream(streams[name]):
+                plan = pa.pa_plan(dims_for(w), d.context_lens, stream=streams[name])
+                out = torch.full_like(d.q, float("nan"))
+                pa.pa_decode(plan, d.q, d.k_cache, d.v_cache, d.block_table, d.context_lens,
+                             s.q_len, s.scale, MODE_CODE[s.kv_scale_mode], d.kv_scales, out,
+                             stream=streams[name])
+                outs[name].append((out, plan))
+    torch.cuda.synchronize()
+    for name in names:
+        for rnd, (out, plan) in enumerate(outs[name]):
+            assert pa.pa_plan_status(plan) == 0
+            assert torch.equal(out.view(torch.int16), refs[name].view(torch.int16)), \
+                f"{name}, round {rnd}"
