@@ -110,8 +110,12 @@ __device__ __forceinline__ float quad_bcast(float x, int i) {
 // for its column (lane % 16). gfx950 permlane swaps exchange rows in VALU:
 // with both operands a copy of x, the 16-lane swap leaves rows (0, 0, 2, 2)
 // in one result and (1, 1, 3, 3) in the other, the 32-lane swap halves
-// (lo, lo) and (hi, hi).
-__device__ __forceinline__ float pick_max(float a, float b) { return a > b ? a : b; }
+// (lo, lo) and (hi, hi). The maximum of two is the median of (a, b, FLT_MAX),
+// one v_med3_f32 (a compare and a select otherwise; with +inf the compiler
+// rewrites it as a maximum that first quiets each operand).
+__device__ __forceinline__ float pick_max(float a, float b) {
+  return __builtin_amdgcn_fmed3f(a, b, 3.40282347e38f);
+}
 
 template <bool kMax>
 __device__ __forceinline__ float rows_reduce(float x) {
@@ -605,7 +609,7 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
   // alternate between two buffers by step; a segment merge puts the waves' O
   // tiles in the stream's two buffers (its first barrier follows every read
   // of them).
-  static_assert(!SH || (RS % 2 == 0 && (2 * NB) % RS == 0),
+  static_assert(!SH || (RS % 2 == 0 && (2 * NB) % RS == 0 && NB % 2 == 0),
                 "shared tiles: an even number of waves, each loading whole blocks");
   constexpr int SHR = SH ? RS : 0;
   constexpr int NBL = Stage<D, FP8, NB, SM, SHR>::NBL;
@@ -613,6 +617,12 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
   static_assert(!SH || RS * C::OBYTES <= 2 * SHBUF, "merge tiles fit the stream's buffers");
   // Prefetch the next segment's Q into registers when they are affordable.
   constexpr bool QPF = RT == 1 || (RT == 2 && NW <= 4);
+  // Shared-tile kernels are bound by instruction issue, so their row sums
+  // come out of the PV MFMAs: one more output tile whose V rows are all ones
+  // (the matrix cores idle most of the step) instead of a VALU add per
+  // probability. The sums are then those of the bf16 probabilities the PV
+  // products take, the values O is the weighted sum of.
+  constexpr bool ONES = SH;
 
   __shared__ __attribute__((aligned(16))) uint8_t lds_waves[SH ? NST * 2 * SHBUF : NW * C::WBYTES];
   __shared__ float st_m[NW][RT * 16];
@@ -706,6 +716,8 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
 
   float m[RT], l[RT];
   f32x4 o[DT][RT];
+  f32x4 ol[ONES ? RT : 1];  // ONES: the row sums, in every element
+  const bf16x8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
 
   // One step of a wave's pipeline, computing ev[0] from stage CUR. Issue
   // order: pages of ev[NE-1], Q of ev[1] if it opens a segment, K/V of
@@ -729,6 +741,7 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
         l[rt] = 0.f;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[dt][rt] = f32x4{0, 0, 0, 0};
+        if constexpr (ONES) ol[rt] = f32x4{0, 0, 0, 0};
       }
     }
     load_pages<NB, OPC>(a, ev[NE - 1], pg[CUR]);
@@ -816,6 +829,7 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
 #pragma unroll
       for (int blk = 0; blk < NB; ++blk) qk[blk] = per_tok ? cs.ks[blk] * qk_f : qk_f;
       float pv[NB][RT][4];
+      float pl[ONES && per_tok ? NB : 1][RT][4];  // ONES, per-token: p before the V scale
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         float x[NB][4];
@@ -850,6 +864,7 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
           l[rt] *= alpha;
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) o[dt][rt] *= alpha;
+          if constexpr (ONES) ol[rt] *= alpha;
           m[rt] = mn;
         }
         const float mu = m[rt] == neg_inf() ? 0.f : m[rt];
@@ -859,11 +874,12 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float p = __builtin_amdgcn_exp2f(x[blk][i] - mu);
-            ps += p;
+            if constexpr (!ONES) ps += p;
+            if constexpr (ONES && per_tok) pl[blk][rt][i] = p;
             pv[blk][rt][i] = per_tok ? p * quad_bcast(cs.vs[blk], i) : p;
           }
         }
-        l[rt] += ps;
+        if constexpr (!ONES) l[rt] += ps;
       }
 
       // ---- V rows -> wave-private LDS tile (row-major bf16); SH, LIN:
@@ -917,6 +933,24 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
             bp[qq][rt] = __builtin_convertvector(f, bf16x8);
           }
         }
+        if constexpr (ONES) {
+          // row sums: ones^T P^T (per-token: the probabilities before the V
+          // scale)
+#pragma unroll
+          for (int qq = 0; qq < NB / 2; ++qq) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+              bf16x8 b = bp[qq][rt];
+              if constexpr (per_tok) {
+                const f32x8 f = {pl[2 * qq][rt][0], pl[2 * qq][rt][1], pl[2 * qq][rt][2], pl[2 * qq][rt][3],
+                                 pl[2 * qq + 1][rt][0], pl[2 * qq + 1][rt][1], pl[2 * qq + 1][rt][2],
+                                 pl[2 * qq + 1][rt][3]};
+                b = __builtin_convertvector(f, bf16x8);
+              }
+              ol[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, b, ol[rt], 0, 0, 0);
+            }
+          }
+        }
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
@@ -937,7 +971,8 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         float v = l[rt];
-        v = rows_reduce<false>(v);
+        if constexpr (ONES) v = ol[rt][0];  // the full row sum, in every lane of column c
+        else v = rows_reduce<false>(v);
         if (j == 0) {
           st_m[wave][16 * rt + c] = m[rt];
           st_l[wave][16 * rt + c] = v;
