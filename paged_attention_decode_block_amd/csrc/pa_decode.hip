@@ -110,14 +110,18 @@ __device__ __forceinline__ float quad_bcast(float x, int i) {
 // for its column (lane % 16). gfx950 permlane swaps exchange rows in VALU:
 // with both operands a copy of x, the 16-lane swap leaves rows (0, 0, 2, 2)
 // in one result and (1, 1, 3, 3) in the other, the 32-lane swap halves
-// (lo, lo) and (hi, hi). The maximum of two is the median of (a, b, FLT_MAX),
-// one v_med3_f32 (a compare and a select otherwise; with +inf the compiler
-// rewrites it as a maximum that first quiets each operand).
+// (lo, lo) and (hi, hi). MED3 takes the maximum of two as the median of
+// (a, b, FLT_MAX): one v_med3_f32 instead of a compare and a select, but the
+// constant holds a scalar register, which the shared-tile kernels can spare
+// and the others cannot without spilling more (with +inf the compiler
+// rewrites the median as a maximum that first quiets each operand).
+template <bool MED3>
 __device__ __forceinline__ float pick_max(float a, float b) {
-  return __builtin_amdgcn_fmed3f(a, b, 3.40282347e38f);
+  if constexpr (MED3) return __builtin_amdgcn_fmed3f(a, b, 3.40282347e38f);
+  return a > b ? a : b;
 }
 
-template <bool kMax>
+template <bool kMax, bool MED3 = false>
 __device__ __forceinline__ float rows_reduce(float x) {
   // (each element is copied to a scalar before the bit cast: a bit cast of a
   // vector element in place reads element 0)
@@ -125,12 +129,12 @@ __device__ __forceinline__ float rows_reduce(float x) {
   const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
   const uint32_t a0u = r16[0], a1u = r16[1];
   const float a0 = __builtin_bit_cast(float, a0u), a1 = __builtin_bit_cast(float, a1u);
-  x = kMax ? pick_max(a0, a1) : a0 + a1;
+  x = kMax ? pick_max<MED3>(a0, a1) : a0 + a1;
   const uint32_t w = __builtin_bit_cast(uint32_t, x);
   const auto r32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);
   const uint32_t b0u = r32[0], b1u = r32[1];
   const float b0 = __builtin_bit_cast(float, b0u), b1 = __builtin_bit_cast(float, b1u);
-  return kMax ? pick_max(b0, b1) : b0 + b1;
+  return kMax ? pick_max<MED3>(b0, b1) : b0 + b1;
 }
 
 // LDS transpose read (gfx950 ds_read_b64_tr_b16). Within each 16-lane group,
@@ -853,7 +857,7 @@ __global__ __launch_bounds__(NW * 64, (NW + 3) / 4) void partition_kernel(Decode
 #pragma unroll
           for (int i = 0; i < 4; ++i) cm = fmaxf(cm, x[blk][i]);
         }
-        cm = rows_reduce<true>(cm);
+        cm = rows_reduce<true, SH>(cm);
         // Lazy rescale: keep the running max m while every row's chunk max
         // stays within 2^kSlack of it (then p <= 2^kSlack, exact enough in
         // fp32 and bf16); move it, rescaling l and O, only when some row of

@@ -50,17 +50,35 @@ def test_records_are_dropped_when_the_sources_change(monkeypatch):
     assert bench.recorded_mfma("no_such_workload") is None
 
 
+def _shared_tile_workloads():
+    """Workloads whose partition kernel (as named in the committed kernel-trace
+    record) shares K/V tiles between waves: its tenth template argument."""
+    out = set()
+    for ln in (ROOT / "profiles" / "pa_kernels_trace_all_workloads.md").read_text().splitlines():
+        f = [x.strip() for x in ln.split("|")]
+        if len(f) > 3 and f[2].startswith("`partition_kernel<"):
+            args = f[2][len("`partition_kernel<"):-2].split(",")
+            if args[9].strip() == "true":
+                out.add(f[1])
+    return out
+
+
 def test_mfma_flops_match_the_padded_tile_count():
     """Executed bf16 MFMA flops per launch (counted on the GPU) = 4 x kv heads
     x head_dim x the query rows of a kv head rounded up to the 16-row MFMA tile
-    x each sequence's tokens rounded up to the kernel's 32-token step."""
+    x each sequence's tokens rounded up to the kernel's 32-token step (QK^T
+    and PV, 2 flops per product each). A shared-tile kernel adds one 16-column
+    PV tile of ones, its row sums: 2 x 16 more per token and row."""
     recs = _records(bench.MFMA_FILE, "mfma")
+    shared = _shared_tile_workloads()
+    assert shared == {"C4_fp8_q4_per_token", "C4_fp8_q4_per_tensor"}
     for name, f in recs.items():
         s = W.CONFIGS[name]
         t = int(((W.draw_context_lens(s, 2026) + 31) // 32 * 32).sum())
         rows = s.q_len * (s.num_q_heads // s.num_kv_heads)
         padded = -(-rows // 16) * 16
-        assert int(f[4]) == 4 * t * s.num_kv_heads * padded * s.head_dim, name
+        cols = 2 * s.head_dim + (16 if name in shared else 0)
+        assert int(f[4]) == 2 * t * s.num_kv_heads * padded * cols, name
 
 
 def test_scale_sweep_shapes_are_valid():
