@@ -136,14 +136,17 @@ def test_bad_context_reports_and_writes_nothing():
 
 
 @pytest.mark.parametrize("scale", [-0.2, 0.0, 1.5])
-@pytest.mark.parametrize("kv", ["bf16", "fp8_tok", "fp8_ten_q4"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8_tok", "fp8_ten_q4", "fp8_tok_q4"])
 def test_softmax_scales(kv, scale):
     # a negative scale (the max tracks the most negative dot product), zero
     # (uniform weights over the visible keys) and a large one (scores spread
-    # over tens of exp2 units, so the lazy rescale moves the running max often)
+    # over tens of exp2 units, so the lazy rescale moves the running max often).
+    # The q_len-4 fp8 kernels share K/V tiles and take their row sums from a
+    # PV tile of ones; per-token, from the probabilities before the V scale.
     spec = {"bf16": W.scaled(W.C3, batch=4, ctx_lo=1, ctx_hi=900, max_ctx=1024),
             "fp8_tok": W.scaled(W.C4_Q1_TOK, batch=3, ctx_lo=1, ctx_hi=2500, max_ctx=3072),
-            "fp8_ten_q4": W.scaled(W.C4_Q4_TEN, batch=3, ctx_lo=4, ctx_hi=2500, max_ctx=3072)}[kv]
+            "fp8_ten_q4": W.scaled(W.C4_Q4_TEN, batch=3, ctx_lo=4, ctx_hi=2500, max_ctx=3072),
+            "fp8_tok_q4": W.scaled(W.C4_Q4_TOK, batch=3, ctx_lo=4, ctx_hi=2500, max_ctx=3072)}[kv]
     w = W.generate(spec, 2029)
     say(f"[decode] scale {scale} {kv} ctx={w.context_lens.tolist()}")
     d = upload(w)
