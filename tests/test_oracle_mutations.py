@@ -1,9 +1,12 @@
 """Planted mistakes in the oracle must fail its pins (no GPU).
 
 Each case patches one plausible slip into a copy of an oracle function — a
-wrong head grouping, an off-by-one causal mask, a dropped scale, a transposed
-page index, a wrong subnormal exponent, unnormalised merge weights, a segment
-counter that ignores the pair — and checks that at least one pin test raises.
+wrong head grouping, an off-by-one or top-left causal mask, a dropped scale,
+a transposed page index, a wrong subnormal exponent, unnormalised merge
+weights, a log-sum-exp in the wrong log base or over unshifted exponentials,
+swapped or logically-paged per-token scales, bf16 ties rounded away from zero
+or rounded twice, a segment counter that ignores the pair, an unclipped last
+partition, ranges rounded up — and checks that at least one pin test raises.
 The patches live only here, on the CPU; the oracle itself is unchanged.
 """
 import numpy as np
@@ -200,3 +203,131 @@ def test_planted_cache_mistake_is_caught(slip, monkeypatch):
         monkeypatch.setattr(cache, "quantise_row", times_scale)
     with pytest.raises(AssertionError):
         _cache_pins()
+
+
+# --------------------------------------------------------------------------- more slips
+
+def _attend_range_with(lse_of, l_of):
+    """attend_range with its log-sum-exp or its normaliser replaced."""
+    def fn(q, k_cache, v_cache, block_table, context_lens, q_len, scale, page_size, b, g, t0, t1,
+           kv_dtype=att.KV_BF16, scale_mode=att.SCALE_NONE, kv_scales=None):
+        ctx, group, Q, K, V = att._pair_inputs(q, k_cache, v_cache, block_table, context_lens, b, g,
+                                               q_len, kv_dtype, scale_mode, kv_scales, page_size)
+        R, D = Q.shape
+        t1 = min(t1, ctx)
+        o = np.zeros((R, D))
+        lse = np.full(R, -np.inf)
+        if t1 <= t0:
+            return o, lse
+        s = scale * (Q @ K[t0:t1].T)
+        vis = att._visible(ctx, q_len, group, t0, t1)
+        for r in range(R):
+            sr = s[r][vis[r]]
+            if sr.size == 0:
+                continue
+            m = sr.max()
+            w = np.exp(sr - m)
+            l = l_of(sr, m, w)
+            o[r] = (w @ V[t0:t1][vis[r]]) / l
+            lse[r] = lse_of(m, l)
+        return o, lse
+    return fn
+
+
+def _visible_top_left(ctx, q_len, group, t0, t1):
+    i = np.arange(q_len * group) // group
+    t = np.arange(t0, t1)
+    return t[None, :] <= i[:, None]                 # slip: query i aligned to key i, not ctx - q_len + i
+
+
+def _scales_k_v_swapped(kv_scales, which, block_table, b, g, ctx, page_size):
+    sc = att._np(kv_scales)
+    bt = att._np(block_table)
+    t = np.arange(ctx)
+    return sc[1 - which, bt[b, t // page_size].astype(np.int64), g, t % page_size].astype(np.float64)
+
+
+def _scales_logical_page(kv_scales, which, block_table, b, g, ctx, page_size):
+    sc = att._np(kv_scales)
+    t = np.arange(ctx)
+    return sc[which, t // page_size, g, t % page_size].astype(np.float64)   # slip: no block table
+
+
+MORE_ATTENTION = {
+    "lse in the log2 domain": (att, "attend_range",
+                               _attend_range_with(lambda m, l: m + np.log2(l), lambda sr, m, w: w.sum())),
+    "partial normalised by the unshifted sum": (att, "attend_range",
+                                                _attend_range_with(lambda m, l: m + np.log(l),
+                                                                   lambda sr, m, w: np.exp(sr).sum())),
+    "causal mask aligned top-left": (att, "_visible", _visible_top_left),
+    "K and V scales swapped": (att, "_gather_scales", _scales_k_v_swapped),
+    "scale page taken from the logical page": (att, "_gather_scales", _scales_logical_page),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MORE_ATTENTION))
+def test_more_planted_attention_mistakes_are_caught(name, monkeypatch):
+    mod, attr, fn = MORE_ATTENTION[name]
+    monkeypatch.setattr(mod, attr, fn)
+    if attr == "attend_range":
+        monkeypatch.setattr(oracle, "attend_range", fn)
+    with pytest.raises(AssertionError):
+        _pins()
+
+
+def _round_bf16_ties_away(x):
+    x = np.asarray(x, dtype=np.float64)
+    out = np.array(x, copy=True)
+    fin = np.isfinite(x) & (x != 0)
+    _, e = np.frexp(x[fin])
+    ulp_exp = np.maximum(e, -125) - 8
+    y = np.ldexp(x[fin], -ulp_exp)
+    out[fin] = np.ldexp(np.trunc(y + np.copysign(0.5, y)), ulp_exp)   # slip: ties away from zero
+    return out
+
+
+def _round_bf16_via_float32(x):
+    x = np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)   # slip: rounds twice
+    return _real_round_bf16(x)
+
+
+_real_round_bf16 = codecs.round_to_bf16
+
+
+@pytest.mark.parametrize("slip", [_round_bf16_ties_away, _round_bf16_via_float32])
+def test_planted_bf16_rounding_mistake_is_caught(slip, monkeypatch):
+    monkeypatch.setattr(codecs, "round_to_bf16", slip)
+    monkeypatch.setattr(oracle, "round_to_bf16", slip)
+    with pytest.raises(AssertionError):
+        T.test_code_points()
+
+
+def _last_item_not_clipped(pl):
+    # slip: every item spans a whole partition, the last one past the context
+    P = None
+    for p, t0, t1, slot in pl.items:
+        if P is None or t1 - t0 > P:
+            P = t1 - t0
+    pl.items = [(p, t0, t0 + P, slot) for p, t0, t1, slot in pl.items]
+
+
+def _ranges_rounded_up(pl):
+    # slip: workgroup w starts at ceil(w N / G)
+    G = len(pl.wg_begin) - 1
+    pl.wg_begin = [-(-w * pl.num_items // G) for w in range(G + 1)]
+
+
+@pytest.mark.parametrize("slip", [_last_item_not_clipped, _ranges_rounded_up])
+def test_planted_plan_range_mistake_is_caught(slip, monkeypatch):
+    real = oracle.plan
+
+    def mutated(*a, **kw):
+        pl = real(*a, **kw)
+        slip(pl)
+        return pl
+    monkeypatch.setattr(oracle, "plan", mutated)
+    with pytest.raises(AssertionError):
+        T.test_worked_example_plans()
+    with pytest.raises(AssertionError):
+        for s in range(40):
+            TP.test_plan_closed_forms_random(s)
